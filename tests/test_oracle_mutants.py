@@ -1,0 +1,144 @@
+"""Plant one plausible mistake at a time in a copy of the oracle (on the CPU) and check that
+at least one pin fails. This is what makes the pins a check of the oracle rather than a
+restatement of it: a dropped term, a wrong sign or index, a transposed operand, a wrong log
+base or mask offset each has to trip something.
+"""
+import numpy as np
+import pytest
+
+import oracle.direct as OA
+from tests import pins
+
+
+def _rows_mutant(kind):
+    def rows(qrows, rows_idx, K, V, causal, offset, scale):
+        Sk = K.shape[0]
+        s = scale
+        if kind == "no_scale":
+            s = 1.0
+        if kind == "scale_sqrt":
+            s = np.sqrt(scale)
+        S = s * (qrows @ K.T)
+        if kind == "wrong_sign":
+            S = -S
+        if causal:
+            keys = np.arange(Sk)[None, :]
+            if kind == "causal_strict":
+                visible = keys < (rows_idx[:, None] + offset)
+            elif kind == "causal_topleft":
+                visible = keys <= rows_idx[:, None]
+            elif kind == "causal_transposed":
+                visible = keys >= (rows_idx[:, None] + offset)
+            else:
+                visible = keys <= (rows_idx[:, None] + offset)
+            if kind != "mask_after_softmax":
+                S = np.where(visible, S, -np.inf)
+        m = S.max(axis=1) if Sk else np.full(S.shape[0], -np.inf)
+        empty = ~np.isfinite(m)
+        m_safe = np.where(empty, 0.0, m)
+        if kind == "no_max_sub":
+            with np.errstate(over="ignore"):
+                P = np.exp(S)
+        elif kind == "exp2":
+            P = np.exp2(S - m_safe[:, None])
+        else:
+            P = np.exp(S - m_safe[:, None])
+        l = P.sum(axis=1)
+        if kind == "mask_after_softmax" and causal:
+            P = np.where(visible, P, 0.0)
+        with np.errstate(invalid="ignore", divide="ignore"):
+            if kind == "no_normalize":
+                O = P @ V
+            elif kind == "values_from_keys":
+                O = (P @ K[:, :V.shape[1]]) / l[:, None] if K.shape[1] >= V.shape[1] else (P @ V) / l[:, None] * 0
+            else:
+                O = (P @ V) / l[:, None]
+            if kind == "lse_log2":
+                lse = m_safe + np.log2(l)
+            elif kind == "lse_no_max":
+                lse = np.log(l)
+            elif kind == "lse_no_log":
+                lse = m_safe + l
+            else:
+                lse = m_safe + np.log(l)
+        O[empty] = 0.0
+        if kind != "empty_lse_zero":
+            lse[empty] = -np.inf
+        else:
+            lse[empty] = 0.0
+        return O, lse
+    return rows
+
+
+ROW_MUTANTS = ["no_scale", "scale_sqrt", "wrong_sign", "causal_strict", "causal_topleft",
+               "causal_transposed", "mask_after_softmax", "no_max_sub", "exp2", "no_normalize",
+               "values_from_keys", "lse_log2", "lse_no_max", "lse_no_log", "empty_lse_zero"]
+
+
+def _gqa_mutant(q, k, v, causal=False, scale=None):
+    """attention() with query head h reading KV head h % Hkv (interleaved, not grouped)."""
+    B, Hq, Sq, D = q.shape
+    Hkv, Sk = k.shape[1], k.shape[2]
+    s = float(np.float32(scale if scale is not None else 1 / np.sqrt(D)))
+    O = np.zeros((B, Hq, Sq, v.shape[3]))
+    L = np.zeros((B, Hq, Sq))
+    for b in range(B):
+        for h in range(Hq):
+            o, lse = OA._rows(q[b, h].astype(np.float64), np.arange(Sq), k[b, h % Hkv],
+                              v[b, h % Hkv], causal, Sk - Sq, s)
+            O[b, h], L[b, h] = o, lse
+    return O, L
+
+
+def _gather_mutant(kind):
+    def gather(cache, block_table, ctx_len, b, block_size):
+        n = ctx_len + 1 if kind == "one_past_end" else ctx_len
+        t = np.arange(n)
+        if kind == "swap_block_slot":
+            phys = block_table[b, t % block_size]
+            slot = t // block_size % block_size
+        elif kind == "table_row_by_slot":
+            phys = block_table[b, np.minimum(t // block_size + (t % block_size == block_size - 1), block_table.shape[1] - 1)]
+            slot = t % block_size
+        elif kind == "physical_is_logical":
+            phys = t // block_size
+            slot = t % block_size
+        else:
+            phys = block_table[b, t // block_size]
+            slot = t % block_size
+        return np.transpose(cache[phys, :, slot, :], (1, 0, 2))
+    return gather
+
+
+def _some_pin_fails():
+    failed = []
+    for pin in pins.ALL_PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin()
+        except (AssertionError, ValueError, IndexError, FloatingPointError):
+            failed.append(pin.__name__)
+    return failed
+
+
+@pytest.mark.parametrize("kind", ROW_MUTANTS)
+def test_row_mutant_is_caught(kind, monkeypatch):
+    monkeypatch.setattr(OA, "_rows", _rows_mutant(kind))
+    assert _some_pin_fails(), f"no pin catches mutant {kind}"
+
+
+def test_unmutated_copy_passes(monkeypatch):
+    monkeypatch.setattr(OA, "_rows", _rows_mutant("none"))
+    assert _some_pin_fails() == []
+
+
+def test_gqa_mutant_is_caught(monkeypatch):
+    monkeypatch.setattr(OA, "attention", _gqa_mutant)
+    assert "pin_gqa" in _some_pin_fails()
+
+
+@pytest.mark.parametrize("kind", ["one_past_end", "swap_block_slot", "table_row_by_slot",
+                                  "physical_is_logical"])
+def test_gather_mutant_is_caught(kind, monkeypatch):
+    monkeypatch.setattr(OA, "gather_paged", _gather_mutant(kind))
+    assert "pin_decode_paged" in _some_pin_fails()

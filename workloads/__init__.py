@@ -1,0 +1,223 @@
+"""Seeded synthetic inputs shared by the oracle checks, the GPU tests and the benchmark.
+
+This module draws and lays out input data only: random normals, their rounding to
+bfloat16, and the paged KV-cache layout with its block table. It contains none of the
+attention arithmetic, so the CPU oracle and the HIP path stay independent of each other
+while still seeing bit-identical inputs.
+
+Workload shapes follow the pages:
+  * the Llama-3-8B-shaped prefill (32 query heads, 8 KV heads, head size 128) matches the
+    projection widths given in "Kernel and Operator Fusion -- Inference Optimization", §5
+    (the horizontal QKV fusion example: 4096 -> 4096 for Q, 4096 -> 1024 for K and V);
+  * the batched B=8, H=32, S=4096 case is the score tensor of more than four billion elements
+    in "Kernel Fusion, Softmax, and Attention", third paragraph;
+  * the 32K-token case is the T x T score matrix of more than a billion entries in
+    "Optimizing Large Language Model Inference Through Kernel Fusion and Advanced Memory
+    Management", §FlashAttention and the Memory-Efficiency Revolution;
+  * the paged decode layout (fixed-size blocks, a block table mapping a sequence's logical
+    blocks to physical ones) is the one in §Paged Attention and Dynamic KV Cache Management
+    of that same article.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+__all__ = [
+    "FwdConfig", "DecodeConfig", "CONFIGS", "bf16_round", "bf16_bits", "bits_to_f32",
+    "fwd_inputs", "decode_inputs", "DecodeInputs", "sample_rows",
+]
+
+
+# ----------------------------------------------------------------------------------------
+# bfloat16 rounding (round to nearest, ties to even) done with integer bit operations.
+# ----------------------------------------------------------------------------------------
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Return the uint16 bfloat16 bit patterns of float32 ``x`` under round-to-nearest-even.
+
+    NaN inputs map to a quiet NaN. Infinities and values that round past the largest finite
+    bfloat16 become infinities, as IEEE rounding requires.
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    lsb = (u >> 16) & 1
+    r = ((u + 0x7FFF + lsb) >> 16).astype(np.uint32)
+    nan = np.isnan(x)
+    if nan.any():
+        r = np.where(nan, ((u >> 16) | 0x40).astype(np.uint32), r)
+    return r.astype(np.uint16)
+
+
+def bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Widen uint16 bfloat16 bit patterns to float32 (exact)."""
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def bf16_round(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to the nearest bfloat16 and return them as (exact) float32."""
+    return bits_to_f32(bf16_bits(x))
+
+
+# ----------------------------------------------------------------------------------------
+# Workload descriptions
+# ----------------------------------------------------------------------------------------
+@dataclass(frozen=True)
+class FwdConfig:
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    Sq: int
+    Sk: int
+    D: int
+    dtype: str          # "bf16" or "f32": the type of Q, K, V and O
+    causal: bool
+    seed: int
+    input_scale: float = 1.0   # N(0,1) draws are multiplied by this before rounding
+    kind: str = field(default="fwd")
+
+    @property
+    def scale(self) -> np.float32:
+        """Softmax scale 1/sqrt(D) as the float32 value handed to the library."""
+        return np.float32(1.0 / math.sqrt(self.D))
+
+
+@dataclass(frozen=True)
+class DecodeConfig:
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    D: int
+    block_size: int
+    ctx_lo: int
+    ctx_hi: int
+    seed: int
+    dtype: str = "bf16"
+    kind: str = field(default="decode")
+
+    @property
+    def scale(self) -> np.float32:
+        return np.float32(1.0 / math.sqrt(self.D))
+
+
+CONFIGS = {
+    "tiny_f32": FwdConfig("tiny_f32", B=1, Hq=1, Hkv=1, Sq=128, Sk=128, D=64,
+                          dtype="f32", causal=False, seed=1001),
+    "llama3_8b_prefill": FwdConfig("llama3_8b_prefill", B=1, Hq=32, Hkv=8, Sq=2048, Sk=2048,
+                                   D=128, dtype="bf16", causal=True, seed=1002),
+    "batched_b8_s4096": FwdConfig("batched_b8_s4096", B=8, Hq=32, Hkv=32, Sq=4096, Sk=4096,
+                                  D=128, dtype="bf16", causal=True, seed=1003),
+    "paged_decode_b64": DecodeConfig("paged_decode_b64", B=64, Hq=32, Hkv=8, D=128,
+                                     block_size=16, ctx_lo=512, ctx_hi=4096, seed=1004),
+    "long_s32768": FwdConfig("long_s32768", B=1, Hq=32, Hkv=8, Sq=32768, Sk=32768, D=128,
+                             dtype="bf16", causal=True, seed=1005, input_scale=0.5),
+}
+
+
+# ----------------------------------------------------------------------------------------
+# Generators
+# ----------------------------------------------------------------------------------------
+def _normal(rng: np.random.Generator, shape, dtype: str, input_scale: float) -> np.ndarray:
+    x = rng.standard_normal(size=shape, dtype=np.float32)
+    if input_scale != 1.0:
+        x *= np.float32(input_scale)
+    if dtype == "bf16":
+        x = bf16_round(x)
+    return x
+
+
+def fwd_inputs(B, Hq, Hkv, Sq, Sk, D, seed, dtype="bf16", input_scale=1.0):
+    """Q [B,Hq,Sq,D], K and V [B,Hkv,Sk,D] as float32 arrays, drawn in the order Q, K, V.
+
+    For ``dtype="bf16"`` every value is already rounded to bfloat16 (RNE), so handing the
+    arrays to either side is exact.
+    """
+    rng = np.random.default_rng(seed)
+    q = _normal(rng, (B, Hq, Sq, D), dtype, input_scale)
+    k = _normal(rng, (B, Hkv, Sk, D), dtype, input_scale)
+    v = _normal(rng, (B, Hkv, Sk, D), dtype, input_scale)
+    return q, k, v
+
+
+def fwd_inputs_for(cfg: FwdConfig):
+    return fwd_inputs(cfg.B, cfg.Hq, cfg.Hkv, cfg.Sq, cfg.Sk, cfg.D, cfg.seed,
+                      cfg.dtype, cfg.input_scale)
+
+
+@dataclass
+class DecodeInputs:
+    q: np.ndarray            # [B, Hq, D] float32 (bf16-exact)
+    k_cache: np.ndarray      # [num_blocks, Hkv, block_size, D] float32 (bf16-exact)
+    v_cache: np.ndarray      # same shape as k_cache
+    block_table: np.ndarray  # [B, max_blocks] int32, -1 past a sequence's last block
+    ctx_lens: np.ndarray     # [B] int32
+    block_size: int
+
+
+POISON_FINITE = np.float32(1.0e4)
+
+
+def decode_inputs(B, Hq, Hkv, D, block_size, ctx_lo, ctx_hi, seed, ctx_lens=None,
+                  poison="finite", dtype="bf16", extra_blocks=0):
+    """Paged KV cache for one-token decode.
+
+    Draw order: context lengths (uniform integers in [ctx_lo, ctx_hi], unless ``ctx_lens``
+    is given), a permutation of the physical block pool, then q, k_cache and v_cache from
+    N(0,1). Sequence b owns ceil(ctx_b / block_size) blocks; its logical block j lives in
+    physical block ``perm[offset_b + j]``. Slots past the end of a sequence's last block are
+    overwritten with ``poison`` ("finite" = 1e4, "nan" = NaN, None = left as drawn), so a
+    kernel that reads them shows it. ``extra_blocks`` adds unused physical blocks to the pool.
+    """
+    rng = np.random.default_rng(seed)
+    if ctx_lens is None:
+        ctx = rng.integers(ctx_lo, ctx_hi, size=B, endpoint=True).astype(np.int32)
+    else:
+        ctx = np.asarray(ctx_lens, dtype=np.int32).copy()
+        assert ctx.shape == (B,)
+    nblk = (ctx.astype(np.int64) + block_size - 1) // block_size
+    pool = int(nblk.sum()) + int(extra_blocks)
+    perm = rng.permutation(pool).astype(np.int32)
+    max_blocks = max(1, int(nblk.max()) if B else 1)
+    table = np.full((B, max_blocks), -1, dtype=np.int32)
+    off = 0
+    for b in range(B):
+        n = int(nblk[b])
+        table[b, :n] = perm[off:off + n]
+        off += n
+    q = _normal(rng, (B, Hq, D), dtype, 1.0)
+    kc = _normal(rng, (pool, Hkv, block_size, D), dtype, 1.0)
+    vc = _normal(rng, (pool, Hkv, block_size, D), dtype, 1.0)
+    if poison is not None:
+        val = POISON_FINITE if poison == "finite" else np.float32(np.nan)
+        for b in range(B):
+            n = int(nblk[b])
+            tail = int(ctx[b]) - (n - 1) * block_size   # valid slots in the last block
+            if n > 0 and tail < block_size:
+                pb = table[b, n - 1]
+                kc[pb, :, tail:, :] = val
+                vc[pb, :, tail:, :] = val
+    return DecodeInputs(q, kc, vc, table, ctx, block_size)
+
+
+def decode_inputs_for(cfg: DecodeConfig, **kw):
+    return decode_inputs(cfg.B, cfg.Hq, cfg.Hkv, cfg.D, cfg.block_size, cfg.ctx_lo,
+                         cfg.ctx_hi, cfg.seed, **kw)
+
+
+def sample_rows(B, Hq, Sq, n, seed, must=()):
+    """Pick ``n`` distinct (b, h, i) query rows to check one by one at full size.
+
+    Always includes the first and last rows of every tile edge listed in ``must`` (pairs of
+    row indices) and the global first and last rows; the rest are uniform random.
+    """
+    rng = np.random.default_rng(seed)
+    picks = {(0, 0, 0), (B - 1, Hq - 1, Sq - 1)}
+    for i in must:
+        if 0 <= i < Sq:
+            picks.add((int(rng.integers(B)), int(rng.integers(Hq)), int(i)))
+    while len(picks) < n:
+        picks.add((int(rng.integers(B)), int(rng.integers(Hq)), int(rng.integers(Sq))))
+    return sorted(picks)

@@ -1,0 +1,259 @@
+"""Python binding of libattn.so, the gfx950 fused exact-attention library.
+
+The functions carry the C ABI's names and only marshal arguments: they check the torch
+tensors' dtype, device, shape and layout, pass raw device pointers and the current HIP
+stream to the library, and turn a nonzero status into :class:`AttnError`. Every step of
+the computation runs in the library's HIP kernels; there is no CPU or PyTorch fallback, and
+importing this package fails loudly when the library has not been built.
+
+torch is used for device memory and streams only.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+__all__ = [
+    "AttnError", "library_path", "load_library",
+    "attn_fwd", "attn_fwd_f32", "attn_decode_paged", "attn_decode_paged_ex",
+    "attn_decode_workspace_bytes", "attn_decode_default_splits", "attn_status_string",
+    "attn_last_error", "attn_release_workspace", "attn_abi_version", "EXPORTED_SYMBOLS",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libattn.so")
+
+# Every symbol include/attn.h declares, with its ctypes signature.
+_P, _I, _F, _Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+_SIGNATURES = {
+    "attn_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P]),
+    "attn_fwd_f32": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P]),
+    "attn_decode_paged": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P]),
+    "attn_decode_paged_ex": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I,
+                                  _I, _P, _Z, _P]),
+    "attn_decode_workspace_bytes": (_Z, [_I, _I, _I, _I]),
+    "attn_decode_default_splits": (_I, []),
+    "attn_status_string": (ctypes.c_char_p, [_I]),
+    "attn_last_error": (ctypes.c_char_p, []),
+    "attn_release_workspace": (None, []),
+    "attn_abi_version": (_I, []),
+}
+EXPORTED_SYMBOLS = tuple(_SIGNATURES)
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"[{status}] {message}")
+        self.status = status
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def _hip_runtimes_mapped():
+    """Distinct libamdhip64 files mapped into this process (Linux only)."""
+    try:
+        with open("/proc/self/maps") as f:
+            return sorted({line.split()[-1] for line in f if "libamdhip64" in line})
+    except OSError:
+        return []
+
+
+def load_library():
+    """Load libattn.so once and attach the C signatures. Raises if it is not built.
+
+    torch is imported first: its bundled HIP runtime has the same soname as the system one
+    libattn.so was linked against, so the dynamic loader then binds libattn.so to the runtime
+    torch already uses. Loading libattn.so first would put two HIP runtimes in the process,
+    and the second one to initialise finds no device."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise ImportError(
+                f"{_LIB_PATH} is missing: build it with `python -m exact_attention_42_amd.build` "
+                "(there is no fallback implementation)")
+        import torch  # noqa: F401  (binds the HIP runtime before libattn.so is loaded)
+        lib = ctypes.CDLL(_LIB_PATH)
+        rts = _hip_runtimes_mapped()
+        if len(rts) > 1:
+            raise ImportError(f"more than one HIP runtime is loaded in this process: {rts}")
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+load_library()
+
+
+# ---------------------------------------------------------------------------------------
+def attn_status_string(status: int) -> str:
+    return load_library().attn_status_string(int(status)).decode()
+
+
+def attn_last_error() -> str:
+    return load_library().attn_last_error().decode()
+
+
+def attn_abi_version() -> int:
+    return load_library().attn_abi_version()
+
+
+def attn_decode_default_splits() -> int:
+    return load_library().attn_decode_default_splits()
+
+
+def attn_decode_workspace_bytes(B: int, Hq: int, D: int, max_splits: int = 0) -> int:
+    return load_library().attn_decode_workspace_bytes(B, Hq, D, max_splits)
+
+
+def attn_release_workspace() -> None:
+    load_library().attn_release_workspace()
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise AttnError(status, f"{attn_status_string(status)}: {attn_last_error()}")
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_ptr(device, stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(int(stream.cuda_stream))
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _need(t, name, dtype, device, shape=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (no CPU path exists)")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _fwd(fn_name, dtype, q, k, v, causal, scale, out, lse, want_lse, stream):
+    torch = _torch()
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, S, D]")
+    B, Hq, Sq, D = q.shape
+    Bk, Hkv, Sk, Dk = k.shape
+    if Bk != B or Dk != D or tuple(v.shape) != (B, Hkv, Sk, D):
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    dev = q.device
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, dtype, dev)
+    if out is None:
+        out = torch.empty((B, Hq, Sq, D), dtype=dtype, device=dev)
+    _need(out, "out", dtype, dev, (B, Hq, Sq, D))
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, dev, (B, Hq, Sq))
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    fn = getattr(load_library(), fn_name)
+    with torch.cuda.device(dev):
+        _check(fn(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Sq, Sk, D,
+                  1 if causal else 0, float(scale), _stream_ptr(dev, stream)))
+    return out, lse
+
+
+def attn_fwd(q, k, v, causal=False, scale=None, out=None, lse=None, want_lse=True, stream=None):
+    """bf16 forward. q [B,Hq,Sq,D], k/v [B,Hkv,Sk,D] (bfloat16, contiguous, same GPU).
+
+    Returns (out [B,Hq,Sq,D] bf16, lse [B,Hq,Sq] fp32 or None). ``scale`` defaults to
+    1/sqrt(D). The work is enqueued on ``stream`` (default: torch's current stream)."""
+    return _fwd("attn_fwd", _torch().bfloat16, q, k, v, causal, scale, out, lse, want_lse, stream)
+
+
+def attn_fwd_f32(q, k, v, causal=False, scale=None, out=None, lse=None, want_lse=True,
+                 stream=None):
+    """fp32 forward; same contract as :func:`attn_fwd` with float32 q, k, v, out."""
+    return _fwd("attn_fwd_f32", _torch().float32, q, k, v, causal, scale, out, lse, want_lse,
+                stream)
+
+
+def _decode_checks(q, k_cache, v_cache, block_table, ctx_lens):
+    torch = _torch()
+    if q.dim() != 3 or k_cache.dim() != 4:
+        raise ValueError("q must be [B, Hq, D] and caches [num_blocks, Hkv, block_size, D]")
+    B, Hq, D = q.shape
+    nb, Hkv, bs, Dk = k_cache.shape
+    if Dk != D or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("cache shapes do not match q")
+    dev = q.device
+    _need(q, "q", torch.bfloat16, dev)
+    _need(k_cache, "k_cache", torch.bfloat16, dev)
+    _need(v_cache, "v_cache", torch.bfloat16, dev)
+    _need(ctx_lens, "ctx_lens", torch.int32, dev, (B,))
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be [B, stride]")
+    _need(block_table, "block_table", torch.int32, dev)
+    return B, Hq, D, nb, Hkv, bs, dev
+
+
+def attn_decode_paged(q, k_cache, v_cache, block_table, ctx_lens, scale=None, out=None,
+                      stream=None):
+    """Paged one-token decode (bf16). The block table's row stride is derived on the device
+    from ctx_lens, so ``block_table`` must be exactly [B, max_b ceil(ctx_b / block_size)]."""
+    torch = _torch()
+    B, Hq, D, nb, Hkv, bs, dev = _decode_checks(q, k_cache, v_cache, block_table, ctx_lens)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev)
+    _need(out, "out", torch.bfloat16, dev, (B, Hq, D))
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    with torch.cuda.device(dev):
+        _check(load_library().attn_decode_paged(
+            _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(ctx_lens), _ptr(out),
+            B, Hq, Hkv, D, bs, float(scale), _stream_ptr(dev, stream)))
+    return out
+
+
+def attn_decode_paged_ex(q, k_cache, v_cache, block_table, ctx_lens, scale=None, out=None,
+                         lse=None, want_lse=True, check_blocks=True, max_splits=0,
+                         workspace=None, stream=None):
+    """Paged decode with the explicit controls of the C ABI: returns (out, lse). The row
+    stride of ``block_table`` is passed explicitly; ``check_blocks`` passes the pool size so
+    out-of-range entries are skipped instead of read; ``workspace`` is an optional uint8
+    device tensor of at least attn_decode_workspace_bytes(B, Hq, D, max_splits) bytes."""
+    torch = _torch()
+    B, Hq, D, nb, Hkv, bs, dev = _decode_checks(q, k_cache, v_cache, block_table, ctx_lens)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev)
+    _need(out, "out", torch.bfloat16, dev, (B, Hq, D))
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, dev, (B, Hq))
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8, dev)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    with torch.cuda.device(dev):
+        _check(load_library().attn_decode_paged_ex(
+            _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(ctx_lens), _ptr(out),
+            _ptr(lse), B, Hq, Hkv, D, bs, float(scale), int(block_table.shape[1]),
+            int(nb) if check_blocks else 0, int(max_splits), _ptr(workspace),
+            int(workspace.numel()) if workspace is not None else 0, _stream_ptr(dev, stream)))
+    return out, lse

@@ -1,0 +1,72 @@
+"""Build libattn.so (the C-ABI library with the gfx950 kernels) in place with hipcc.
+
+Run ``python -m exact_attention_42_amd.build`` or call :func:`build`. The library is written
+next to this file; the sources are ``csrc/*.hip`` and the public header ``include/attn.h``.
+"""
+from __future__ import annotations
+
+import concurrent.futures as cf
+import glob
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libattn.so")
+ARCH = "gfx950"
+
+# -packed-fp32-ops: keep the compiler from forming packed fp32 VALU instructions.
+HIPCC_FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+]
+
+
+def _hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found: the HIP toolchain is required to build libattn.so")
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    out = (r.stdout or "") + (r.stderr or "")
+    # the host pass does not know the packed-fp32 feature name; that warning is expected
+    lines = [l for l in out.splitlines() if "not a recognized feature for this target" not in l]
+    if r.returncode != 0:
+        raise RuntimeError(f"command failed ({r.returncode}): {' '.join(cmd)}\n" + "\n".join(lines))
+    if verbose and lines:
+        print("\n".join(lines), flush=True)
+
+
+def build(verbose: bool = False, extra_flags=()) -> str:
+    """Compile every csrc/*.hip for gfx950 and link libattn.so. Returns the library path."""
+    hipcc = _hipcc()
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    if not srcs:
+        raise RuntimeError(f"no HIP sources under {CSRC}")
+    objdir = os.path.join(PKG, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    objs = [os.path.join(objdir, os.path.basename(s)[:-4] + ".o") for s in srcs]
+    flags = HIPCC_FLAGS + list(extra_flags) + ["-I", INCLUDE, "-I", CSRC]
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        futs = [ex.submit(_run, [hipcc] + flags + ["-c", s, "-o", o], verbose)
+                for s, o in zip(srcs, objs)]
+        for f in futs:
+            f.result()
+    tmp = LIB + ".tmp"
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs, verbose)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    path = build(verbose="-v" in sys.argv)
+    print(path)

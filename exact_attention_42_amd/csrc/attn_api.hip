@@ -1,0 +1,256 @@
+// C ABI of libattn.so: argument checks, error reporting, the decode workspace and dispatch
+// to the gfx950 kernels. Declarations and the full contract are in include/attn.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <map>
+#include <mutex>
+#include <string>
+#include <utility>
+
+#include "attn.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return ATTN_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int hip_fail(hipError_t e, const char* where) {
+  return fail(ATTN_ERR_HIP, "%s: %s (%d)", where, hipGetErrorString(e), (int)e);
+}
+
+int check_scale(float scale) {
+  if (!std::isfinite(scale) || scale < 0.f)
+    return fail(ATTN_ERR_SCALE, "scale must be finite and >= 0 (got %g)", (double)scale);
+  return ATTN_OK;
+}
+
+// Returns ATTN_OK and sets *empty when there is nothing to compute.
+int check_fwd(const void* q, const void* k, const void* v, void* o, const float* lse, int B,
+              int Hq, int Hkv, int Sq, int Sk, int D, float scale, bool* empty) {
+  *empty = false;
+  if (B < 0 || Sq < 0 || Sk < 0)
+    return fail(ATTN_ERR_SHAPE, "B, Sq, Sk must be >= 0 (B=%d Sq=%d Sk=%d)", B, Sq, Sk);
+  if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0)
+    return fail(ATTN_ERR_SHAPE, "need Hq >= 1, Hkv >= 1 and Hq %% Hkv == 0 (Hq=%d Hkv=%d)",
+                Hq, Hkv);
+  if (D != 64 && D != 128)
+    return fail(ATTN_ERR_UNSUPPORTED, "head dimension D=%d not supported (64 or 128)", D);
+  if (int rc = check_scale(scale)) return rc;
+  if ((long long)B * Hq > 0x7fffffffLL || (long long)Sq > (1 << 30) || (long long)Sk > (1 << 30))
+    return fail(ATTN_ERR_SHAPE, "problem too large (B*Hq=%lld, Sq=%d, Sk=%d)",
+                (long long)B * Hq, Sq, Sk);
+  if (B == 0 || Sq == 0) {
+    *empty = true;
+    return ATTN_OK;
+  }
+  if (!q || !o) return fail(ATTN_ERR_NULL, "q and o must not be NULL");
+  if (Sk > 0 && (!k || !v)) return fail(ATTN_ERR_NULL, "k and v must not be NULL when Sk > 0");
+  if (!aligned(q, 16) || !aligned(o, 16) || !aligned(k, 16) || !aligned(v, 16))
+    return fail(ATTN_ERR_ALIGN, "q, k, v and o must be 16-byte aligned");
+  if (lse && !aligned(lse, 4)) return fail(ATTN_ERR_ALIGN, "lse must be 4-byte aligned");
+  return ATTN_OK;
+}
+
+int run_fwd(bool f32, const void* q, const void* k, const void* v, void* o, float* lse, int B,
+            int Hq, int Hkv, int Sq, int Sk, int D, int causal, float scale, void* stream) {
+  bool empty;
+  if (int rc = check_fwd(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, &empty)) return rc;
+  if (empty) return ok();
+  attn::FwdProblem p{q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, causal ? 1 : 0, scale};
+  hipError_t e = f32 ? attn::launch_fwd_f32(p, static_cast<hipStream_t>(stream))
+                     : attn::launch_fwd_bf16(p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, f32 ? "attn_fwd_f32 launch" : "attn_fwd launch");
+  return ok();
+}
+
+// ---- decode workspace owned by the library: one buffer per (device, stream) ----
+struct Workspace {
+  void* ptr = nullptr;
+  size_t bytes = 0;
+};
+std::mutex g_ws_mutex;
+std::map<std::pair<int, void*>, Workspace> g_ws;
+
+int default_splits() {
+  static int v = [] {
+    const char* s = std::getenv("ATTN_DECODE_SPLITS");
+    int x = s ? std::atoi(s) : 0;
+    return (x >= 1 && x <= 64) ? x : 16;
+  }();
+  return v;
+}
+
+size_t ws_bytes(int B, int Hq, int D, int splits) {
+  // partial outputs first (16-byte aligned start), then the partial log-sum-exps
+  return attn::decode_workspace_floats(B, Hq, D, splits) * sizeof(float);
+}
+
+int get_workspace(void* stream, size_t need, void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  Workspace& w = g_ws[{dev, stream}];
+  if (w.bytes < need) {
+    if (w.ptr) {
+      e = hipFree(w.ptr);   // synchronises: in-flight kernels may still read the old buffer
+      w.ptr = nullptr;
+      w.bytes = 0;
+      if (e != hipSuccess) return hip_fail(e, "hipFree(workspace)");
+    }
+    size_t sz = need < (1u << 20) ? (1u << 20) : need;
+    e = hipMalloc(&w.ptr, sz);
+    if (e != hipSuccess) {
+      w.ptr = nullptr;
+      (void)hipGetLastError();
+      return fail(ATTN_ERR_NOMEM, "decode workspace of %zu bytes: %s", sz, hipGetErrorString(e));
+    }
+    w.bytes = sz;
+  }
+  *out = w.ptr;
+  return ATTN_OK;
+}
+
+int run_decode(const void* q, const void* k_cache, const void* v_cache,
+               const int32_t* block_table, const int32_t* ctx_lens, void* o, float* lse, int B,
+               int Hq, int Hkv, int D, int block_size, float scale, int table_stride,
+               int num_blocks, int max_splits, void* workspace, size_t workspace_bytes,
+               void* stream) {
+  if (B < 0) return fail(ATTN_ERR_SHAPE, "B must be >= 0 (B=%d)", B);
+  if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0)
+    return fail(ATTN_ERR_SHAPE, "need Hq >= 1, Hkv >= 1 and Hq %% Hkv == 0 (Hq=%d Hkv=%d)",
+                Hq, Hkv);
+  if (B > 65535 || Hkv > 65535)
+    return fail(ATTN_ERR_SHAPE, "B and Hkv must be <= 65535 (B=%d Hkv=%d)", B, Hkv);
+  if (Hq / Hkv > 16)
+    return fail(ATTN_ERR_UNSUPPORTED, "decode supports Hq/Hkv <= 16 (got %d)", Hq / Hkv);
+  if (D != 64 && D != 128)
+    return fail(ATTN_ERR_UNSUPPORTED, "head dimension D=%d not supported (64 or 128)", D);
+  if (block_size != 16)
+    return fail(ATTN_ERR_UNSUPPORTED, "block_size=%d not supported (16)", block_size);
+  if (int rc = check_scale(scale)) return rc;
+  if (max_splits < 0 || max_splits > 64)
+    return fail(ATTN_ERR_SHAPE, "max_splits must be in 0..64 (got %d)", max_splits);
+  const int splits = max_splits ? max_splits : default_splits();
+  if (B == 0) return ok();
+  if (!q || !k_cache || !v_cache || !block_table || !ctx_lens || !o)
+    return fail(ATTN_ERR_NULL, "q, k_cache, v_cache, block_table, ctx_lens and o must not be NULL");
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(o, 16))
+    return fail(ATTN_ERR_ALIGN, "q, k_cache, v_cache and o must be 16-byte aligned");
+  if (!aligned(block_table, 4) || !aligned(ctx_lens, 4) || (lse && !aligned(lse, 4)))
+    return fail(ATTN_ERR_ALIGN, "block_table, ctx_lens and lse must be 4-byte aligned");
+  const size_t need = ws_bytes(B, Hq, D, splits);
+  void* ws = workspace;
+  if (ws) {
+    if (workspace_bytes < need)
+      return fail(ATTN_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed",
+                  workspace_bytes, need);
+    if (!aligned(ws, 16)) return fail(ATTN_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+  } else if (int rc = get_workspace(stream, need, &ws)) {
+    return rc;
+  }
+  attn::DecodeProblem p;
+  p.q = q; p.k_cache = k_cache; p.v_cache = v_cache;
+  p.block_table = block_table; p.ctx_lens = ctx_lens; p.o = o; p.lse = lse;
+  p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.D = D; p.block_size = block_size;
+  p.table_stride = table_stride; p.num_blocks = num_blocks; p.max_splits = splits;
+  p.scale = scale;
+  p.ws_o = static_cast<float*>(ws);
+  p.ws_lse = p.ws_o + (size_t)B * Hq * splits * D;
+  hipError_t e = attn::launch_decode_paged(p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "attn_decode_paged launch");
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+             int Hkv, int Sq, int Sk, int D, int causal, float scale, void* stream) {
+  return run_fwd(false, q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, causal, scale, stream);
+}
+
+int attn_fwd_f32(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                 int Hq, int Hkv, int Sq, int Sk, int D, int causal, float scale, void* stream) {
+  return run_fwd(true, q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, causal, scale, stream);
+}
+
+int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_table, const int32_t* ctx_lens, void* o, int B,
+                      int Hq, int Hkv, int D, int block_size, float scale, void* stream) {
+  return run_decode(q, k_cache, v_cache, block_table, ctx_lens, o, nullptr, B, Hq, Hkv, D,
+                    block_size, scale, 0, 0, 0, nullptr, 0, stream);
+}
+
+int attn_decode_paged_ex(const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* block_table, const int32_t* ctx_lens, void* o,
+                         float* lse, int B, int Hq, int Hkv, int D, int block_size,
+                         float scale, int table_stride, int num_blocks, int max_splits,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  return run_decode(q, k_cache, v_cache, block_table, ctx_lens, o, lse, B, Hq, Hkv, D,
+                    block_size, scale, table_stride, num_blocks, max_splits, workspace,
+                    workspace_bytes, stream);
+}
+
+size_t attn_decode_workspace_bytes(int B, int Hq, int D, int max_splits) {
+  if (B < 0 || Hq < 0 || D < 0 || max_splits < 0 || max_splits > 64) return 0;
+  return ws_bytes(B, Hq, D, max_splits ? max_splits : default_splits());
+}
+
+int attn_decode_default_splits(void) { return default_splits(); }
+
+const char* attn_status_string(int status) {
+  switch (status) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_NULL: return "null pointer";
+    case ATTN_ERR_SHAPE: return "invalid shape";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported configuration";
+    case ATTN_ERR_ALIGN: return "misaligned pointer";
+    case ATTN_ERR_SCALE: return "invalid scale";
+    case ATTN_ERR_HIP: return "HIP runtime error";
+    case ATTN_ERR_NOMEM: return "out of device memory";
+    case ATTN_ERR_WORKSPACE: return "invalid workspace";
+    default: return "unknown status";
+  }
+}
+
+const char* attn_last_error(void) { return g_last_error.c_str(); }
+
+void attn_release_workspace(void) {
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  int cur = 0;
+  bool have_cur = hipGetDevice(&cur) == hipSuccess;
+  for (auto& kv : g_ws) {
+    if (kv.second.ptr) {
+      if (hipSetDevice(kv.first.first) == hipSuccess) (void)hipFree(kv.second.ptr);
+    }
+  }
+  g_ws.clear();
+  if (have_cur) (void)hipSetDevice(cur);
+}
+
+int attn_abi_version(void) { return 1; }
+
+}  // extern "C"

@@ -1,0 +1,47 @@
+// Internal launch interface between the C ABI (attn_api.hip) and the kernel files.
+// Every launcher assumes its arguments were validated by the C ABI and only enqueues work.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace attn {
+
+struct FwdProblem {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;      // may be null
+  int B, Hq, Hkv, Sq, Sk, D;
+  int causal;
+  float scale;
+};
+
+// bf16 Q/K/V/O, fp32 LSE; MFMA kernel. D in {64, 128}.
+hipError_t launch_fwd_bf16(const FwdProblem& p, hipStream_t stream);
+// fp32 Q/K/V/O, fp32 LSE; vector-ALU kernel. D in {64, 128}.
+hipError_t launch_fwd_f32(const FwdProblem& p, hipStream_t stream);
+
+struct DecodeProblem {
+  const void* q;            // [B, Hq, D] bf16
+  const void* k_cache;      // [num_blocks, Hkv, block_size, D] bf16
+  const void* v_cache;
+  const int32_t* block_table;  // [B, table_stride] int32
+  const int32_t* ctx_lens;     // [B] int32
+  void* o;                  // [B, Hq, D] bf16
+  float* lse;               // [B, Hq] fp32 or null
+  int B, Hq, Hkv, D, block_size;
+  int table_stride;         // <= 0: derived on the device as max_b ceil(ctx_b / block_size)
+  int num_blocks;           // <= 0: unknown (no physical-block range check)
+  int max_splits;           // split-KV partitions per sequence (upper bound)
+  float scale;
+  float* ws_o;              // [B, Hq, max_splits, D] fp32 partial outputs
+  float* ws_lse;            // [B, Hq, max_splits] fp32 partial log-sum-exps
+};
+
+size_t decode_workspace_floats(int B, int Hq, int D, int max_splits);
+hipError_t launch_decode_paged(const DecodeProblem& p, hipStream_t stream);
+
+}  // namespace attn

@@ -1,0 +1,127 @@
+/* Fused exact attention for AMD Instinct MI355X (gfx950): C ABI of libattn.so.
+ *
+ * What is computed. For every batch b, query head h and query row i,
+ *     O[b,h,i,:] = sum_j softmax_j( scale * q[b,h,i,:] . k[b,hk,j,:] + mask[i,j] ) v[b,hk,j,:]
+ *     LSE[b,h,i] = ln sum_j exp( scale * q[b,h,i,:] . k[b,hk,j,:] + mask[i,j] )
+ * with hk = h / (Hq / Hkv). This is the attention equation of "Fused Kernel Compiler"
+ * (Candle paper), §FlashAttention Integration, with the scale passed explicitly (1/sqrt(d_k)
+ * in the usual case) and an optional causal mask (the "scale, mask, softmax" pattern of that
+ * page's table "Kernel fusion opportunities"). It is computed in a single pass over K/V with
+ * an online softmax, so no score or probability matrix is ever written to memory (same
+ * section; also "Optimizing Large Language Model Inference Through Kernel Fusion and Advanced
+ * Memory Management", §FlashAttention and the Memory-Efficiency Revolution). Results equal
+ * the plain definition up to floating-point rounding order.
+ *
+ * Conventions shared by every call:
+ *   - All tensors are dense, row-major, in device memory owned by the caller; the library
+ *     never allocates, frees or retains them.
+ *   - q, o: [B, Hq, Sq, D]; k, v: [B, Hkv, Sk, D]; lse: [B, Hq, Sq] float32.
+ *   - Grouped-query attention: Hq must be a multiple of Hkv; query head h uses KV head
+ *     h / (Hq / Hkv) (contiguous groups).
+ *   - causal != 0 masks key j for query i unless j <= i + (Sk - Sq) (aligned to the bottom
+ *     right corner; the usual lower triangle when Sq == Sk). A row that sees no key gets
+ *     O = 0 and LSE = -inf.
+ *   - scale must be finite and >= 0 (scale 0 gives uniform weights over the visible keys).
+ *     scale * |score| must stay finite in float32.
+ *   - Softmax statistics and accumulation are float32 on every path.
+ *   - stream is a hipStream_t (NULL = the null stream). Calls only enqueue work on it and
+ *     never synchronise; faults inside a kernel surface at the caller's next synchronisation.
+ *   - Every argument is checked on the host before anything is launched; on any error the
+ *     call returns a nonzero ATTN_* code, launches nothing and records a message that
+ *     attn_last_error() returns on the calling thread.
+ *   - B == 0, Sq == 0 (or, for decode, B == 0) is a valid empty problem: nothing is launched.
+ *   - The calls are thread-safe.
+ */
+#ifndef EXACT_ATTENTION_ATTN_H
+#define EXACT_ATTENTION_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum attn_status {
+  ATTN_OK = 0,
+  ATTN_ERR_NULL = 1,         /* a required pointer is NULL */
+  ATTN_ERR_SHAPE = 2,        /* negative size, Hq or Hkv < 1, Hq % Hkv != 0, size overflow */
+  ATTN_ERR_UNSUPPORTED = 3,  /* D not in {64, 128}; block_size != 16; decode Hq/Hkv > 16 */
+  ATTN_ERR_ALIGN = 4,        /* q/k/v/o/cache pointer not 16-byte aligned, or lse/table/ctx
+                                pointer not 4-byte aligned */
+  ATTN_ERR_SCALE = 5,        /* scale is NaN, infinite or negative */
+  ATTN_ERR_HIP = 6,          /* the HIP runtime reported an error (text in attn_last_error) */
+  ATTN_ERR_NOMEM = 7,        /* the decode workspace could not be allocated */
+  ATTN_ERR_WORKSPACE = 8     /* caller workspace too small or misaligned */
+};
+
+/* Prefill / full-sequence forward, bfloat16 q, k, v, o (float32 lse).
+ * lse may be NULL (not written). Layouts and semantics as above. D in {64, 128}. */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int B, int Hq, int Hkv, int Sq, int Sk, int D,
+             int causal, float scale, void* stream);
+
+/* The same computation with float32 q, k, v, o (full-precision path). */
+int attn_fwd_f32(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int B, int Hq, int Hkv, int Sq, int Sk, int D,
+                 int causal, float scale, void* stream);
+
+/* One-token decode over a paged KV cache ("Optimizing Large Language Model Inference ...",
+ * §Paged Attention and Dynamic KV Cache Management: fixed-size blocks of the cache are placed
+ * anywhere in a physical pool and a block table maps each sequence's logical blocks to them).
+ *   q, o:      [B, Hq, D] bfloat16 (the newest token of each sequence)
+ *   k_cache, v_cache: [num_blocks, Hkv, block_size, D] bfloat16; token t of sequence b is
+ *              slot t % block_size of physical block block_table[b, t / block_size]
+ *   block_table: [B, stride] int32. Here stride = max_b ceil(ctx_lens[b] / block_size),
+ *              derived on the device (no host synchronisation). Entries at or past a
+ *              sequence's last block are never read.
+ *   ctx_lens:  [B] int32, number of cached tokens of each sequence (the new token included).
+ *              Values <= 0 give O = 0. No mask is applied inside the context.
+ * block_size must be 16. Hq / Hkv must be at most 16. The call runs two kernels on stream:
+ * a split-KV kernel writing per-split partial results to a library-owned workspace (one per
+ * device and stream, grown on demand; growing it synchronises the device) and a combine
+ * kernel merging them by their log-sum-exps. The caller must keep physical block ids valid;
+ * they are not range-checked here (attn_decode_paged_ex can check them). */
+int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_table, const int32_t* ctx_lens, void* o,
+                      int B, int Hq, int Hkv, int D, int block_size, float scale,
+                      void* stream);
+
+/* attn_decode_paged with explicit controls:
+ *   lse:             [B, Hq] float32 log-sum-exp per head, or NULL
+ *   table_stride:    row stride of block_table in entries; <= 0 derives it as above
+ *   num_blocks:      size of the physical pool; > 0 makes the kernels skip (treat as empty)
+ *                    any block-table entry outside [0, num_blocks); <= 0 = unchecked
+ *   max_splits:      upper bound on split-KV partitions per sequence, 1..64; 0 = default
+ *   workspace:       caller-owned device buffer of at least
+ *                    attn_decode_workspace_bytes(B, Hq, D, max_splits) bytes, 16-byte
+ *                    aligned; NULL = use the library-owned workspace */
+int attn_decode_paged_ex(const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* block_table, const int32_t* ctx_lens, void* o,
+                         float* lse, int B, int Hq, int Hkv, int D, int block_size,
+                         float scale, int table_stride, int num_blocks, int max_splits,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of split workspace the decode needs (max_splits 0 = the default). */
+size_t attn_decode_workspace_bytes(int B, int Hq, int D, int max_splits);
+
+/* Default split-KV bound used when max_splits is 0. */
+int attn_decode_default_splits(void);
+
+/* Static text for a status code. */
+const char* attn_status_string(int status);
+
+/* Detail of the last failed call on this thread ("" if none). */
+const char* attn_last_error(void);
+
+/* Frees the library-owned decode workspaces (synchronises the devices that hold them). */
+void attn_release_workspace(void);
+
+/* ABI version of this header: 1. */
+int attn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EXACT_ATTENTION_ATTN_H */

@@ -1,0 +1,162 @@
+"""Paged-decode parity on the GPU: attn_decode_paged / attn_decode_paged_ex (split-KV kernel +
+LSE-merge combine) against the fp64 oracle, plus the invariances the paged layout implies."""
+import numpy as np
+import pytest
+import torch
+
+import exact_attention_42_amd as A
+import oracle
+import workloads as W
+from tests.parity import check_bf16, check_lse, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return torch.device("cuda:0")
+
+
+def upload(d, dev):
+    bf = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev).to(torch.bfloat16)
+    i32 = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+    return bf(d.q), bf(d.k_cache), bf(d.v_cache), i32(d.block_table), i32(d.ctx_lens)
+
+
+def test_config_paged_decode_b64(dev):
+    """B=64, Hq=32, Hkv=8, D=128, ctx uniform in [512, 4096], 16-token blocks placed by a
+    seeded permutation, tail slots poisoned with 1e4: every output element."""
+    cfg = W.CONFIGS["paged_decode_b64"]
+    d = W.decode_inputs_for(cfg)
+    q, kc, vc, bt, ctx = upload(d, dev)
+    o = A.attn_decode_paged(q, kc, vc, bt, ctx, scale=float(cfg.scale))
+    o2, lse = A.attn_decode_paged_ex(q, kc, vc, bt, ctx, scale=float(cfg.scale))
+    torch.cuda.synchronize()
+    O, L = oracle.decode_paged(d.q, d.k_cache, d.v_cache, d.block_table, d.ctx_lens,
+                               cfg.block_size, scale=cfg.scale)
+    mx, mn = check_bf16(to_np(o), O)
+    assert torch.equal(o, o2)
+    err = check_lse(to_np(lse), L)
+    print(f"paged_decode_b64: O max {mx:.3e} mean {mn:.3e}; LSE max {err:.3e}")
+
+
+@pytest.mark.parametrize("ctx", [[1, 15, 16, 17], [31, 32, 33, 1000], [4096, 1, 2, 3]])
+@pytest.mark.parametrize("D,Hq,Hkv", [(128, 32, 8), (64, 8, 8), (128, 16, 1)])
+def test_decode_edge_lengths(ctx, D, Hq, Hkv, dev):
+    d = W.decode_inputs(B=len(ctx), Hq=Hq, Hkv=Hkv, D=D, block_size=16, ctx_lo=0, ctx_hi=0,
+                        seed=sum(ctx) + D, ctx_lens=ctx)
+    q, kc, vc, bt, cl = upload(d, dev)
+    o, lse = A.attn_decode_paged_ex(q, kc, vc, bt, cl)
+    torch.cuda.synchronize()
+    O, L = oracle.decode_paged(d.q, d.k_cache, d.v_cache, d.block_table, d.ctx_lens, 16)
+    check_bf16(to_np(o), O)
+    check_lse(to_np(lse), L)
+
+
+def test_decode_nan_poisoned_tails_are_never_read(dev):
+    d = W.decode_inputs(B=16, Hq=32, Hkv=8, D=128, block_size=16, ctx_lo=1, ctx_hi=300,
+                        seed=77, poison="nan")
+    q, kc, vc, bt, cl = upload(d, dev)
+    o, lse = A.attn_decode_paged_ex(q, kc, vc, bt, cl)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(o).all())
+    O, L = oracle.decode_paged(d.q, d.k_cache, d.v_cache, d.block_table, d.ctx_lens, 16)
+    check_bf16(to_np(o), O)
+    check_lse(to_np(lse), L)
+
+
+def test_decode_block_permutation_is_bitwise_invariant(dev):
+    d = W.decode_inputs(B=8, Hq=32, Hkv=8, D=128, block_size=16, ctx_lo=100, ctx_hi=900, seed=5)
+    q, kc, vc, bt, cl = upload(d, dev)
+    o1, l1 = A.attn_decode_paged_ex(q, kc, vc, bt, cl)
+    pool = kc.shape[0]
+    perm = torch.randperm(pool, generator=torch.Generator().manual_seed(3)).to(dev)
+    inv = torch.empty_like(perm)
+    inv[perm] = torch.arange(pool, device=dev)
+    kc2 = torch.empty_like(kc)
+    vc2 = torch.empty_like(vc)
+    kc2[inv] = kc
+    vc2[inv] = vc
+    bt2 = torch.where(bt >= 0, inv[bt.clamp(min=0)].to(torch.int32), bt)
+    o2, l2 = A.attn_decode_paged_ex(q, kc2, vc2, bt2, cl)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 8, 64])
+def test_decode_split_count_invariance(splits, dev):
+    d = W.decode_inputs(B=12, Hq=32, Hkv=8, D=128, block_size=16, ctx_lo=1, ctx_hi=2000, seed=6)
+    q, kc, vc, bt, cl = upload(d, dev)
+    o, lse = A.attn_decode_paged_ex(q, kc, vc, bt, cl, max_splits=splits)
+    torch.cuda.synchronize()
+    O, L = oracle.decode_paged(d.q, d.k_cache, d.v_cache, d.block_table, d.ctx_lens, 16)
+    check_bf16(to_np(o), O)
+    check_lse(to_np(lse), L)
+
+
+def test_decode_matches_last_row_of_causal_prefill(dev):
+    """Decode of token n over a paged copy of K/V equals row n of causal prefill (both on the
+    GPU, both within the bf16 tolerance of the oracle and of each other)."""
+    Hq, Hkv, D, n = 32, 8, 128, 777
+    q, k, v = W.fwd_inputs(1, Hq, Hkv, n, n, D, seed=12)
+    bf = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev).to(torch.bfloat16)
+    of, _ = A.attn_fwd(bf(q), bf(k), bf(v), causal=True)
+    nblk = (n + 15) // 16
+    rng = np.random.default_rng(0)
+    perm = rng.permutation(nblk + 5).astype(np.int32)
+    kc = np.zeros((nblk + 5, Hkv, 16, D), dtype=np.float32)
+    vc = np.zeros_like(kc)
+    for t in range(n):
+        kc[perm[t // 16], :, t % 16] = k[0, :, t]
+        vc[perm[t // 16], :, t % 16] = v[0, :, t]
+    bt = perm[:nblk][None].copy()
+    od, ld = A.attn_decode_paged_ex(bf(q[:, :, -1]), bf(kc), bf(vc),
+                                    torch.from_numpy(bt).to(dev),
+                                    torch.tensor([n], dtype=torch.int32, device=dev))
+    torch.cuda.synchronize()
+    check_bf16(to_np(od)[0], to_np(of)[0, :, -1], max_abs=2e-2)
+    O, L = oracle.attention(q, k, v, causal=True)
+    check_bf16(to_np(od)[0], O[0, :, -1])
+
+
+def test_decode_out_of_range_blocks_are_skipped_when_checked(dev):
+    d = W.decode_inputs(B=3, Hq=8, Hkv=2, D=128, block_size=16, ctx_lo=40, ctx_hi=40, seed=8)
+    q, kc, vc, bt, cl = upload(d, dev)
+    bad = bt.clone()
+    bad[1, 1] = 10 ** 6        # logical block 1 of sequence 1 points outside the pool
+    o, lse = A.attn_decode_paged_ex(q, kc, vc, bad, cl, check_blocks=True)
+    torch.cuda.synchronize()
+    # sequence 1 then attends to its blocks 0 and 2 only: tokens 0-15 and 32-39
+    keep = np.r_[0:16, 32:40]
+    tbl = d.block_table
+    K = oracle.gather_paged(d.k_cache, tbl, 40, 1, 16)[:, keep][None]
+    V = oracle.gather_paged(d.v_cache, tbl, 40, 1, 16)[:, keep][None]
+    O1, L1 = oracle.attention(d.q[1][None, :, None, :], K, V)
+    check_bf16(to_np(o)[1], O1[0, :, 0])
+    O, L = oracle.decode_paged(d.q, d.k_cache, d.v_cache, tbl, d.ctx_lens, 16)
+    check_bf16(to_np(o)[[0, 2]], O[[0, 2]])
+
+
+def test_decode_zero_context_and_caller_workspace(dev):
+    d = W.decode_inputs(B=4, Hq=8, Hkv=2, D=64, block_size=16, ctx_lo=1, ctx_hi=100, seed=9,
+                        ctx_lens=[0, 50, 0, 17])
+    q, kc, vc, bt, cl = upload(d, dev)
+    nbytes = A.attn_decode_workspace_bytes(4, 8, 64, 4)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    o, lse = A.attn_decode_paged_ex(q, kc, vc, bt, cl, max_splits=4, workspace=ws)
+    torch.cuda.synchronize()
+    O, L = oracle.decode_paged(d.q, d.k_cache, d.v_cache, d.block_table, d.ctx_lens, 16)
+    check_bf16(to_np(o), O)
+    check_lse(to_np(lse), L)
+    assert bool((o[[0, 2]] == 0).all())
+
+
+def test_decode_is_deterministic(dev):
+    d = W.decode_inputs(B=16, Hq=32, Hkv=8, D=128, block_size=16, ctx_lo=500, ctx_hi=3000,
+                        seed=10)
+    q, kc, vc, bt, cl = upload(d, dev)
+    ref, ref_l = A.attn_decode_paged_ex(q, kc, vc, bt, cl)
+    for _ in range(30):
+        o, l = A.attn_decode_paged_ex(q, kc, vc, bt, cl)
+        assert torch.equal(o, ref) and torch.equal(l, ref_l)

@@ -1,0 +1,190 @@
+"""Forward parity on the GPU: the HIP kernels behind attn_fwd / attn_fwd_f32 against the
+fp64 oracle on identical seeded inputs (rounded to bf16 first for the bf16 path).
+
+Small shapes are compared element by element over every output and span several 128-query
+and 64-key tiles plus ragged tails; the full-size workloads are compared on sampled rows that
+the oracle computes one by one, and on properties that hold at any size.
+"""
+import numpy as np
+import pytest
+import torch
+
+import exact_attention_42_amd as A
+import oracle
+import workloads as W
+from tests.parity import check_bf16, check_f32, check_lse, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return torch.device("cuda:0")
+
+
+def _gpu(x, dev, dtype):
+    return torch.from_numpy(np.ascontiguousarray(x)).to(dev).to(dtype)
+
+
+def run_bf16(q, k, v, causal, scale, dev):
+    o, lse = A.attn_fwd(_gpu(q, dev, torch.bfloat16), _gpu(k, dev, torch.bfloat16),
+                        _gpu(v, dev, torch.bfloat16), causal=causal, scale=float(scale))
+    torch.cuda.synchronize()
+    return to_np(o), to_np(lse)
+
+
+SMALL = [
+    # B, Hq, Hkv, Sq, Sk, D, causal
+    (1, 1, 1, 128, 128, 128, False),
+    (1, 1, 1, 128, 128, 128, True),
+    (2, 4, 2, 200, 200, 128, True),       # ragged q and k tails, GQA 2:1
+    (2, 4, 2, 200, 200, 128, False),
+    (1, 8, 2, 333, 333, 64, True),        # D = 64, GQA 4:1
+    (1, 2, 2, 257, 257, 64, False),
+    (1, 2, 1, 100, 300, 128, True),       # Sq < Sk: bottom-right causal alignment
+    (1, 2, 1, 300, 100, 128, True),       # Sq > Sk: the first 200 rows see no key
+    (1, 2, 2, 1, 777, 128, True),         # one query, a decode-like row
+    (1, 2, 2, 70, 1, 128, False),         # one key
+    (3, 2, 1, 129, 63, 64, False),        # Sk below one tile
+    (1, 4, 4, 512, 512, 128, True),       # several full tiles, MHA
+]
+
+
+@pytest.mark.parametrize("shape", SMALL, ids=lambda s: "x".join(map(str, s)))
+def test_fwd_bf16_small(shape, dev):
+    B, Hq, Hkv, Sq, Sk, D, causal = shape
+    q, k, v = W.fwd_inputs(B, Hq, Hkv, Sq, Sk, D, seed=hash(shape) % 2**31)
+    scale = np.float32(1 / np.sqrt(D))
+    o, lse = run_bf16(q, k, v, causal, scale, dev)
+    O, L = oracle.attention(q, k, v, causal=causal, scale=scale)
+    check_bf16(o, O)
+    check_lse(lse, L)
+
+
+@pytest.mark.parametrize("shape", [(1, 1, 1, 128, 128, 64, False), (2, 4, 2, 200, 150, 128, True),
+                                   (1, 2, 1, 77, 300, 64, True), (1, 2, 2, 300, 90, 128, True)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_fwd_f32_small(shape, dev):
+    B, Hq, Hkv, Sq, Sk, D, causal = shape
+    q, k, v = W.fwd_inputs(B, Hq, Hkv, Sq, Sk, D, seed=7 + Sq, dtype="f32")
+    scale = np.float32(1 / np.sqrt(D))
+    o, lse = A.attn_fwd_f32(_gpu(q, dev, torch.float32), _gpu(k, dev, torch.float32),
+                            _gpu(v, dev, torch.float32), causal=causal, scale=float(scale))
+    torch.cuda.synchronize()
+    O, L = oracle.attention(q, k, v, causal=causal, scale=scale)
+    check_f32(to_np(o), O)
+    check_lse(to_np(lse), L, tol=1e-5)
+
+
+def test_config_tiny_f32(dev):
+    """B=1, H=1, S=128, D=64, fp32, non-causal: every output element."""
+    cfg = W.CONFIGS["tiny_f32"]
+    q, k, v = W.fwd_inputs_for(cfg)
+    o, lse = A.attn_fwd_f32(_gpu(q, dev, torch.float32), _gpu(k, dev, torch.float32),
+                            _gpu(v, dev, torch.float32), causal=cfg.causal, scale=float(cfg.scale))
+    torch.cuda.synchronize()
+    O, L = oracle.attention(q, k, v, causal=cfg.causal, scale=cfg.scale)
+    check_f32(to_np(o), O)
+    check_lse(to_np(lse), L, tol=1e-5)
+
+
+def test_config_llama3_8b_prefill_full(dev):
+    """B=1, Hq=32, Hkv=8, S=2048, D=128, bf16, causal: every output element."""
+    cfg = W.CONFIGS["llama3_8b_prefill"]
+    q, k, v = W.fwd_inputs_for(cfg)
+    o, lse = run_bf16(q, k, v, cfg.causal, cfg.scale, dev)
+    O, L = oracle.attention(q, k, v, causal=cfg.causal, scale=cfg.scale)
+    mx, mn = check_bf16(o, O)
+    err = check_lse(lse, L)
+    print(f"llama3_8b_prefill: O max {mx:.3e} mean {mn:.3e}; LSE max {err:.3e}")
+
+
+def _full_size_check(name, dev, nrows=384):
+    cfg = W.CONFIGS[name]
+    q, k, v = W.fwd_inputs_for(cfg)
+    qg, kg, vg = (_gpu(x, dev, torch.bfloat16) for x in (q, k, v))
+    o, lse = A.attn_fwd(qg, kg, vg, causal=cfg.causal, scale=float(cfg.scale))
+    torch.cuda.synchronize()
+    # properties at every position: finite; each O row is a convex combination of V rows
+    assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(lse).all())
+    g = cfg.Hq // cfg.Hkv
+    vmax = vg.float().amax(dim=2).repeat_interleave(g, dim=1)    # [B, Hq, D]
+    vmin = vg.float().amin(dim=2).repeat_interleave(g, dim=1)
+    assert bool((o.float() <= vmax[:, :, None, :] + 2e-2).all())
+    assert bool((o.float() >= vmin[:, :, None, :] - 2e-2).all())
+    # causal row 0 sees key 0 only: O = V_0 rounded, LSE = scale * q_0 . k_0
+    # sampled rows, including both sides of every tile edge that the samples touch
+    edges = [0, 1, 63, 64, 127, 128, 129, 255, 256, cfg.Sq - 129, cfg.Sq - 128, cfg.Sq - 2,
+             cfg.Sq - 1]
+    rows = W.sample_rows(cfg.B, cfg.Hq, cfg.Sq, nrows, seed=cfg.seed, must=edges)
+    O, L = oracle.attention_rows(q, k, v, rows, causal=cfg.causal, scale=cfg.scale)
+    idx = tuple(np.array(rows).T)
+    o_np = o.float().cpu().numpy()
+    lse_np = lse.cpu().numpy()
+    mx, mn = check_bf16(o_np[idx], O, what=f"{name} sampled O")
+    err = check_lse(lse_np[idx], L, what=f"{name} sampled LSE")
+    print(f"{name}: {len(rows)} rows: O max {mx:.3e} mean {mn:.3e}; LSE max {err:.3e}")
+
+
+def test_config_batched_b8_s4096_sampled(dev):
+    """B=8, H=32, S=4096, D=128, bf16, causal at full size."""
+    _full_size_check("batched_b8_s4096", dev)
+
+
+def test_config_long_s32768_sampled(dev):
+    """B=1, Hq=32, Hkv=8, S=32768, D=128, bf16 x0.5, causal at full size."""
+    _full_size_check("long_s32768", dev, nrows=256)
+
+
+def test_scale_zero_and_no_keys(dev):
+    q, k, v = W.fwd_inputs(1, 2, 1, 130, 90, 128, seed=5)
+    o, lse = run_bf16(q, k, v, True, np.float32(0.0), dev)
+    O, L = oracle.attention(q, k, v, causal=True, scale=0.0)
+    check_bf16(o, O)
+    check_lse(lse, L)
+    # Sk = 0: every row sees nothing
+    qg = _gpu(q, dev, torch.bfloat16)
+    e = torch.empty((1, 1, 0, 128), dtype=torch.bfloat16, device=dev)
+    o, lse = A.attn_fwd(qg, e, e, causal=False)
+    torch.cuda.synchronize()
+    assert bool((o == 0).all()) and bool(torch.isneginf(lse).all())
+
+
+def test_empty_problems(dev):
+    e = torch.empty((0, 4, 16, 128), dtype=torch.bfloat16, device=dev)
+    o, lse = A.attn_fwd(e, e[:, :2], e[:, :2])
+    assert o.shape == (0, 4, 16, 128)
+    q = torch.empty((1, 4, 0, 64), dtype=torch.bfloat16, device=dev)
+    k = torch.zeros((1, 2, 5, 64), dtype=torch.bfloat16, device=dev)
+    o, lse = A.attn_fwd(q, k, k, causal=True)
+    torch.cuda.synchronize()
+    assert o.shape == (1, 4, 0, 64)
+
+
+def test_fwd_is_deterministic(dev):
+    """Repeated launches give identical bits (guards the LDS double buffer against races)."""
+    q, k, v = W.fwd_inputs(2, 8, 2, 640, 640, 128, seed=9)
+    qg, kg, vg = (_gpu(x, dev, torch.bfloat16) for x in (q, k, v))
+    ref, ref_l = A.attn_fwd(qg, kg, vg, causal=True)
+    for _ in range(30):
+        o, l = A.attn_fwd(qg, kg, vg, causal=True)
+        assert torch.equal(o, ref) and torch.equal(l, ref_l)
+
+
+def test_gqa_equals_repeated_heads(dev):
+    q, k, v = W.fwd_inputs(1, 8, 2, 300, 300, 128, seed=10)
+    qg, kg, vg = (_gpu(x, dev, torch.bfloat16) for x in (q, k, v))
+    o1, l1 = A.attn_fwd(qg, kg, vg, causal=True)
+    o2, l2 = A.attn_fwd(qg, kg.repeat_interleave(4, 1).contiguous(),
+                        vg.repeat_interleave(4, 1).contiguous(), causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_causal_row0_is_v0(dev):
+    q, k, v = W.fwd_inputs(2, 4, 2, 256, 256, 128, seed=11)
+    qg, kg, vg = (_gpu(x, dev, torch.bfloat16) for x in (q, k, v))
+    o, lse = A.attn_fwd(qg, kg, vg, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o[:, :, 0], vg.repeat_interleave(2, 1)[:, :, 0])

@@ -1,0 +1,225 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused exact-attention hot path on one MI355X.
+
+One step is one pass of the whole hot path over one batch of synthetic input:
+  * prefill: attn_fwd on the Llama-3-8B-shaped workload (B=1, Hq=32, Hkv=8, S=2048, D=128,
+    bf16, causal), then
+  * decode:  attn_decode_paged on the paged workload (B=64, Hq=32, Hkv=8, D=128, contexts
+    uniform in [512, 4096], 16-token blocks placed by a seeded permutation), which runs the
+    split-KV kernel and the LSE-merge combine kernel.
+Inputs are generated once, uploaded, and resident in HBM before timing starts.
+
+Printed (one JSON line): ``value`` is the prefill kernel's throughput in TFLOP/s counting
+4*D flops per visible (query, key) pair (causal-adjusted); ``decode`` gives the decode KV
+bandwidth in GB/s counting each visible token's K and V once plus q, o and the block table.
+Kernel durations come from HIP events recorded around each launch on the launch stream.
+``roofline`` compares the prefill kernel with the bf16 dense MFMA peak, ``decode.roofline``
+the decode with the HBM peak. ``cpu_baseline`` times the fp64 CPU oracle on the host on the
+same prefill workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import workloads as W  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (256 CUs x 4096 flop/clk x 2.4 GHz)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PREFILL = W.CONFIGS["llama3_8b_prefill"]
+DECODE = W.CONFIGS["paged_decode_b64"]
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "exact_attention_42_amd", "csrc")
+
+
+def prefill_flops(cfg) -> float:
+    """4*D flops per visible (query, key) pair: QK^T and PV each 2*D per pair."""
+    Sq, Sk = cfg.Sq, cfg.Sk
+    if cfg.causal:
+        i = np.arange(Sq, dtype=np.int64)
+        visible = int(np.clip(i + (Sk - Sq) + 1, 0, Sk).sum())
+    else:
+        visible = Sq * Sk
+    return 4.0 * cfg.B * cfg.Hq * cfg.D * visible
+
+
+def decode_bytes(ctx_lens, cfg) -> float:
+    """Each visible token's K and V once per KV head, plus q, o and the block table rows."""
+    kv = float(np.sum(ctx_lens, dtype=np.int64)) * 2 * cfg.Hkv * cfg.D * 2
+    qo = 2 * cfg.B * cfg.Hq * cfg.D * 2
+    nblk = (np.asarray(ctx_lens, dtype=np.int64) + cfg.block_size - 1) // cfg.block_size
+    table = float(nblk.sum()) * 4 + cfg.B * 4
+    return kv + qo + table
+
+
+def source_digest(*names) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(CSRC, n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel_tag: str, digest: str):
+    """HBM bytes per launch from a committed counter summary, if it was taken on the current
+    kernel source (its digest line matches); otherwise None."""
+    path = os.path.join(PROFILES, f"{kernel_tag}_counters.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_d = re.search(r"kernel_source_digest:\s*([0-9a-f]+)", text)
+    m_t = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_d or not m_t or m_d.group(1) != digest:
+        return None
+    return float(m_t.group(1))
+
+
+def cpu_baseline(min_seconds: float):
+    """The fp64 oracle (as it stands) on the prefill workload, repeated until min_seconds."""
+    import oracle
+    from threadpoolctl import threadpool_info
+    q, k, v = W.fwd_inputs_for(PREFILL)
+    flops = prefill_flops(PREFILL)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.attention(q, k, v, causal=PREFILL.causal, scale=PREFILL.scale)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds:
+            break
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": flops * reps / el / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"full llama3_8b_prefill workload (32 heads x 2048 x 2048, causal, fp64 "
+                      f"numpy, dense score rows) x {reps} in {el:.1f} s; host cpus "
+                      f"{os.cpu_count()}, affinity {len(os.sched_getaffinity(0))}"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="minimum host time for the oracle baseline (0 skips it)")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="also run one plain device copy of this size (for counter scaling)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE {world})", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import exact_attention_42_amd as A
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    bf = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev).to(torch.bfloat16)
+
+    q, k, v = W.fwd_inputs_for(PREFILL)
+    qg, kg, vg = bf(q), bf(k), bf(v)
+    del q, k, v
+    o = torch.empty_like(qg)
+    lse = torch.empty(qg.shape[:3], dtype=torch.float32, device=dev)
+    d = W.decode_inputs_for(DECODE)
+    dq, dkc, dvc = bf(d.q), bf(d.k_cache), bf(d.v_cache)
+    dbt = torch.from_numpy(d.block_table).to(dev)
+    dctx = torch.from_numpy(d.ctx_lens).to(dev)
+    do = torch.empty_like(dq)
+    ctx_lens = d.ctx_lens.copy()
+    del d
+    scale_p, scale_d = float(PREFILL.scale), float(DECODE.scale)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        A.attn_fwd(qg, kg, vg, causal=True, scale=scale_p, out=o, lse=lse)
+        if ev is not None:
+            ev[1].record()
+        A.attn_decode_paged(dq, dkc, dvc, dbt, dctx, scale=scale_d, out=do)
+        if ev is not None:
+            ev[2].record()
+
+    if args.calibrate_copy_mib > 0:
+        n = args.calibrate_copy_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    for _ in range(args.warmup):
+        step()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+
+    fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
+    dec_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    flops = prefill_flops(PREFILL)
+    tflops = flops / (fwd_ms * 1e-3) / 1e12
+    dbytes = decode_bytes(ctx_lens, DECODE)
+    gbs = dbytes / (dec_ms * 1e-3) / 1e9
+
+    fwd_digest = source_digest("attn_fwd_bf16.hip", "cdna4.hpp")
+    dec_digest = source_digest("attn_decode.hip", "cdna4.hpp")
+    out = {
+        "metric": "fwd attention TFLOP/s & % MFMA peak (prefill); decode KV GB/s & % HBM peak",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) inputs rounded to bf16; seeds 1002 and 1004)",
+        "config": {
+            "workload": "llama3_8b_prefill: B=1 Hq=32 Hkv=8 S=2048 D=128 causal bf16 "
+                        "+ paged_decode_b64: B=64 Hq=32 Hkv=8 D=128 ctx U[512,4096] "
+                        "block 16",
+            "prefill_flops_per_launch": flops,
+            "decode_bytes_per_launch": dbytes,
+            "sum_ctx": int(np.sum(ctx_lens)),
+        },
+        "prefill": {"kernel_ms": round(fwd_ms, 5), "tflops": round(tflops, 2),
+                    "frac_of_peak": round(tflops / PEAK_BF16_TFLOPS, 4)},
+        "decode": {"kernel_ms": round(dec_ms, 5), "value": round(gbs, 1), "unit": "GB/s",
+                   "roofline": {"bound": "hbm", "achieved": round(gbs, 1),
+                                "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                "frac": round(gbs / PEAK_HBM_GBS, 4),
+                                "traffic": measured_traffic("decode_split_paged_decode_b64",
+                                                            dec_digest)}},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic("fwd_bf16_llama3_8b_prefill", fwd_digest)},
+        "kernel_source_digest": {"fwd": fwd_digest, "decode": dec_digest},
+    }
+    if args.cpu_seconds > 0:
+        out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -7,6 +7,7 @@ from __future__ import annotations
 
 import concurrent.futures as cf
 import glob
+import hashlib
 import os
 import shutil
 import subprocess
@@ -46,13 +47,13 @@ def _run(cmd, verbose):
         print("\n".join(lines), flush=True)
 
 
-def build(verbose: bool = False, extra_flags=()) -> str:
-    """Compile every csrc/*.hip for gfx950 and link libattn.so. Returns the library path."""
+def build(verbose: bool = False, extra_flags=(), out: str = LIB) -> str:
+    """Compile every csrc/*.hip for gfx950 and link libattn.so (or ``out``). Returns its path."""
     hipcc = _hipcc()
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     if not srcs:
         raise RuntimeError(f"no HIP sources under {CSRC}")
-    objdir = os.path.join(PKG, "_build")
+    objdir = os.path.join(PKG, "_build", hashlib.sha1(" ".join(extra_flags).encode()).hexdigest()[:8])
     os.makedirs(objdir, exist_ok=True)
     objs = [os.path.join(objdir, os.path.basename(s)[:-4] + ".o") for s in srcs]
     flags = HIPCC_FLAGS + list(extra_flags) + ["-I", INCLUDE, "-I", CSRC]
@@ -61,10 +62,10 @@ def build(verbose: bool = False, extra_flags=()) -> str:
                 for s, o in zip(srcs, objs)]
         for f in futs:
             f.result()
-    tmp = LIB + ".tmp"
+    tmp = out + ".tmp"
     _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs, verbose)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -31,7 +31,10 @@ using namespace cdna4;
 constexpr int kBS = 16;              // tokens per cache block
 constexpr int kDecThreads = 256;
 constexpr int kDecWaves = 4;
-constexpr int kMinBlocksPerSplit = 8;
+#ifndef ATTN_DEC_MIN_BPS
+#define ATTN_DEC_MIN_BPS 8
+#endif
+constexpr int kMinBlocksPerSplit = ATTN_DEC_MIN_BPS;
 constexpr int kMaxGroup = 16;        // query heads per KV head handled by one MFMA column set
 
 struct DecArgs {

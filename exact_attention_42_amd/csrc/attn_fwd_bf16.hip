@@ -29,6 +29,13 @@ namespace {
 
 using namespace cdna4;
 
+#ifndef ATTN_FWD_WAVES_PER_EU
+#define ATTN_FWD_WAVES_PER_EU 2
+#endif
+#ifndef ATTN_FWD_ZIGZAG
+#define ATTN_FWD_ZIGZAG 0
+#endif
+
 constexpr int kBM = 128;
 constexpr int kBN = 64;
 constexpr int kThreads = 256;
@@ -127,7 +134,9 @@ __device__ __forceinline__ void store_tile(const TileRegs<D>& r, char* stage, in
 }
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(FwdArgs a) {
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(ATTN_FWD_WAVES_PER_EU, ATTN_FWD_WAVES_PER_EU)))
+void fwd_bf16_kernel(FwdArgs a) {
   using L = FwdLds<D>;
   constexpr int KS = D / 16;        // MFMA k-steps over the head dimension
   constexpr int DB = D / 32;        // 32-wide d blocks of O^T
@@ -144,7 +153,14 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(FwdArgs a) {
   const int id = blockIdx.x;
   const int rank = id / BH;
   const int bh = id - rank * BH;
-  const int tile = CAUSAL ? (a.ntq - 1 - rank) : rank;
+  int tile = rank;
+  if (CAUSAL) {
+    // heaviest tiles first; with ZIGZAG the second half of the ranks runs lightest-first,
+    // so the two workgroups that share a CU early on carry complementary amounts of work
+    const int half = (a.ntq + 1) / 2;
+    if (ATTN_FWD_ZIGZAG && rank >= half) tile = rank - half;
+    else tile = a.ntq - 1 - rank;
+  }
   const int b = bh / a.Hq;
   const int hq = bh - b * a.Hq;
   const int hk = hq / a.group;

@@ -279,6 +279,11 @@ def pin_brute_force():
         Od, Ld = _decimal_attention(q, k, v, causal, 0.6)
         _close(O, Od, 1e-13, f"brute force O {Hq, Hkv, Sq, Sk, causal}")
         _close(L, Ld, 1e-13, f"brute force LSE {Hq, Hkv, Sq, Sk, causal}")
+        rows = [(0, h, i) for h in range(Hq) for i in (0, Sq // 2, Sq - 1)]
+        Or, Lr = OA.attention_rows(q, k, v, rows, causal=causal, scale=0.6)
+        idx = tuple(np.array(rows).T)
+        _close(Or, Od[idx], 1e-13, f"brute force sampled rows O {Hq, Hkv, Sq, Sk, causal}")
+        _close(Lr, Ld[idx], 1e-13, f"brute force sampled rows LSE {Hq, Hkv, Sq, Sk, causal}")
 
 
 # --- P7/P8/P9/P10: invariances ----------------------------------------------------------

@@ -13,10 +13,19 @@
 // sum are per lane: a row max needs one exchange with lane l^32, and P^T leaves the first
 // product's accumulators in exactly the B-operand layout of the second (no LDS round trip).
 //
-// K/V tiles of 64 keys are staged through LDS, double-buffered: the global loads for tile
-// j+1 are in flight while tile j is consumed. K is stored row-major with a 16-byte row pad;
-// V is transposed on the way in (V^T rows of 64 keys, 8-byte granules XOR-swizzled) so the
-// PV operand reads are two ds_read_b64 per MFMA without bank conflicts.
+// K/V staging: tiles of 64 keys go from global memory straight into LDS with direct-to-LDS
+// loads (global_load_lds_dwordx4: each lane's 16 bytes land at base + 16*lane), double
+// buffered, so no registers or ALU work are spent on staging. Rows are stored unpadded with
+// their 16-byte chunks XOR-permuted; each lane fetches the global chunk that belongs in its
+// LDS slot. The K permutation (chunk ^ row%16) makes the row-per-lane ds_read_b128 operand
+// reads conflict-free; V stays row-major and its V^T operand comes from the transposing read
+// ds_read_b64_tr_b16 (each group of 16 lanes turns 4 keys x 16 columns into 16 lanes x 4
+// keys), with the V permutation (chunk ^ 4*(row%4)) spreading those reads over all banks.
+//
+// Softmax: base 2 with scale*log2(e) folded into one FMA per score. The running reference
+// max is only moved when a row's max exceeds it by more than 2^8 (lazy rescale): until then
+// the probabilities are at most 256, far from overflow, and the result is the same up to
+// rounding, while the O accumulators are rescaled only a handful of times per row.
 //
 // Causal masking is bottom-right aligned (key j visible to query i iff j <= i + Sk - Sq);
 // tiles wholly above the diagonal are never loaded, and 32-key blocks above a wave's
@@ -32,25 +41,33 @@ using namespace cdna4;
 #ifndef ATTN_FWD_WAVES_PER_EU
 #define ATTN_FWD_WAVES_PER_EU 2
 #endif
-#ifndef ATTN_FWD_ZIGZAG
-#define ATTN_FWD_ZIGZAG 0
-#endif
 
 constexpr int kBM = 128;
 constexpr int kBN = 64;
 constexpr int kThreads = 256;
+constexpr float kLazy = 8.0f;      // log2 of the largest probability allowed before rescaling
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 template <int D>
-struct FwdLds {
-  static constexpr int kPitch = D * 2 + 16;        // K row: D bf16 + 16 B pad
-  static constexpr int kKBytes = kBN * kPitch;
-  static constexpr int kVBytes = D * kBN * 2;      // V^T: D rows x 64 keys bf16
-  static constexpr int kStage = kKBytes + kVBytes;
-  static constexpr int kTotal = 2 * kStage;
+struct Geo {
+  static constexpr int kRow = 2 * D;              // bytes per K or V row in LDS
+  static constexpr int kTile = kBN * kRow;        // one K or V tile
+  static constexpr int kCPR = D / 8;              // 16-byte chunks per row
+  static constexpr int kRPI = 1024 / kRow;        // rows per 1 KiB direct load
+  static constexpr int kIPW = kTile / 1024 / 4;   // direct loads per wave, per tensor, per tile
+  static constexpr int KS = D / 16;               // MFMA k-steps over the head dimension
+  static constexpr int DB = D / 32;               // 32-wide d blocks of O^T
 };
 
-// Position of the 8-byte granule g (keys 4g..4g+3) inside V^T row d.
-__device__ __forceinline__ int vt_swz(int d) { return (d & 15) ^ (((d >> 4) & 3) << 2); }
+// Chunk permutations (XOR masks) of K and V rows in LDS.
+template <int D>
+__device__ __forceinline__ int kswz(int row) { return row % (D / 8); }
+template <int D>
+__device__ __forceinline__ int vswz(int row) {
+  return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1);
+}
 
 struct FwdArgs {
   const uint16_t* q;
@@ -65,70 +82,142 @@ struct FwdArgs {
   float c;         // scale * log2(e), > 0
 };
 
+// Issue this wave's share of the direct-to-LDS loads of the K/V tile at key kt. Keys past
+// Sk are clamped to Sk-1: they are masked out of the scores, and their (finite) V rows are
+// multiplied by a probability of exactly 0.
 template <int D>
-struct TileRegs {
-  // global -> LDS staging registers for one K/V tile
-  static constexpr int kKLoads = D / 32;           // 16-byte K chunks per thread
-  u32x4 kreg[kKLoads];
-  u32x4 vreg[4];
-};
-
-template <int D>
-__device__ __forceinline__ void load_tile(TileRegs<D>& r, const uint16_t* kbase,
-                                          const uint16_t* vbase, int kt, int Sk, int tid) {
-  constexpr int CPR = D / 8;                 // 16-byte chunks per row
-  constexpr int RPP = kThreads / CPR;        // rows per pass
-  const int c = tid % CPR;
+__device__ __forceinline__ void dma_tile(char* sk, char* sv, const uint16_t* kbase,
+                                         const uint16_t* vbase, int kt, int Sk, int wave,
+                                         int lane) {
+  using G = Geo<D>;
+  const int pos = lane % G::kCPR;
+  const int rsub = lane / G::kCPR;
 #pragma unroll
-  for (int i = 0; i < TileRegs<D>::kKLoads; ++i) {
-    const int row = tid / CPR + RPP * i;
-    const int key = kt + row;
-    if (key < Sk)
-      r.kreg[i] = *reinterpret_cast<const u32x4*>(kbase + (size_t)key * D + c * 8);
-    else
-      r.kreg[i] = u32x4{0, 0, 0, 0};
-  }
-  // V: thread (dc, kg) reads keys 4kg..4kg+3 at d-chunk dc
-  const int dc = tid % CPR;
-  const int kg = tid / CPR;
-  if (kg < 16) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = kt + 4 * kg + i;
-      if (key < Sk)
-        r.vreg[i] = *reinterpret_cast<const u32x4*>(vbase + (size_t)key * D + dc * 8);
-      else
-        r.vreg[i] = u32x4{0, 0, 0, 0};
-    }
+  for (int i = 0; i < G::kIPW; ++i) {
+    const int blk = wave * G::kIPW + i;
+    const int row = blk * G::kRPI + rsub;
+    const size_t key = (size_t)min(kt + row, Sk - 1);
+    const uint16_t* kp = kbase + key * D + ((pos ^ kswz<D>(row)) * 8);
+    const uint16_t* vp = vbase + key * D + ((pos ^ vswz<D>(row)) * 8);
+    __builtin_amdgcn_global_load_lds(kp, (lds_void*)(sk + blk * 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(vp, (lds_void*)(sv + blk * 1024), 16, 0, 0);
   }
 }
 
+__device__ __forceinline__ void wait_dma_and_barrier() {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+}
+
 template <int D>
-__device__ __forceinline__ void store_tile(const TileRegs<D>& r, char* stage, int tid) {
-  using L = FwdLds<D>;
-  constexpr int CPR = D / 8;
-  constexpr int RPP = kThreads / CPR;
-  const int c = tid % CPR;
+struct WaveState {
+  using G = Geo<D>;
+  u32x4 qf[G::KS];          // Q^T fragments (B operand)
+  f32x16 o[G::DB];          // O^T accumulators
+  float mref;               // reference max (scaled, base 2) of this lane's query
+  float l_run;              // sum of probabilities over this lane's half of the keys
+  int koff[G::KS];          // per-lane K operand offsets within a tile
+  int voff[G::DB];          // per-lane V^T transposed-read offsets within a tile
+};
+
+// One K/V tile: S^T = K Q^T, mask, online softmax, O^T += V^T P^T.
+template <int D, bool CAUSAL>
+__device__ __forceinline__ void compute_tile(WaveState<D>& w, const char* sk, const char* sv,
+                                             int kt, int Sk, int qw, int wave_last_key,
+                                             int my_q, int off, int h, float c) {
+  using G = Geo<D>;
+  bool act[2];
 #pragma unroll
-  for (int i = 0; i < TileRegs<D>::kKLoads; ++i) {
-    const int row = tid / CPR + RPP * i;
-    *reinterpret_cast<u32x4*>(stage + row * L::kPitch + c * 16) = r.kreg[i];
+  for (int kb = 0; kb < 2; ++kb)
+    act[kb] = (kt + 32 * kb < Sk) && (!CAUSAL || kt + 32 * kb <= wave_last_key);
+
+  // ---- S^T = K Q^T ----
+  f32x16 s[2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    if (act[kb]) {
+      const char* kr = sk + 32 * kb * G::kRow;
+      s[kb] = mfma32x32x16(*reinterpret_cast<const u32x4*>(kr + w.koff[0]), w.qf[0], f32x16{});
+#pragma unroll
+      for (int kk = 1; kk < G::KS; ++kk)
+        s[kb] = mfma32x32x16(*reinterpret_cast<const u32x4*>(kr + w.koff[kk]), w.qf[kk], s[kb]);
+    } else {
+      // a block no query of this wave can see (it is masked below in any case)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kb][r] = -INFINITY;
+    }
   }
-  const int dc = tid % CPR;
-  const int kg = tid / CPR;
-  if (kg < 16) {
-    char* vt = stage + L::kKBytes;
-    // transpose the 4 keys x 8 d block: for each d, the 4 keys form one 8-byte granule
+
+  // ---- mask: causal diagonal, key tail, inactive blocks ----
+  const bool need_mask = (kt + kBN > Sk) || (CAUSAL && kt + kBN - 1 > qw + off);
+  if (need_mask) {
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const uint32_t a = r.vreg[0][w], b = r.vreg[1][w], cc = r.vreg[2][w], dd = r.vreg[3][w];
-      // d = 8dc + 2w (low halves) and 8dc + 2w + 1 (high halves)
-      const int d0 = 8 * dc + 2 * w;
-      const int d1 = d0 + 1;
-      u32x2 g0 = {pack_lo16(a, b), pack_lo16(cc, dd)};
-      u32x2 g1 = {pack_hi16(a, b), pack_hi16(cc, dd)};
-      *reinterpret_cast<u32x2*>(vt + d0 * (kBN * 2) + ((kg ^ vt_swz(d0)) * 8)) = g0;
-      *reinterpret_cast<u32x2*>(vt + d1 * (kBN * 2) + ((kg ^ vt_swz(d1)) * 8)) = g1;
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = kt + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
+        bool vis = act[kb] && key < Sk;
+        if (CAUSAL) vis = vis && (key <= my_q + off);
+        s[kb][r] = vis ? s[kb][r] : -INFINITY;
+      }
+    }
+  }
+
+  // ---- online softmax (per lane = per query) with a lazily moved reference ----
+  float mx = -INFINITY;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) mx = fmax3(mx, s[kb][r], s[kb][r + 1]);
+  mx = fmaxf(mx, wave_xor(mx, 32));
+  const float mxc = mx * c;                       // -inf stays -inf (c > 0)
+  const bool move = mxc > w.mref + kLazy;
+  if (__builtin_amdgcn_ballot_w64(move)) {
+    // lanes that keep their reference use 1 (not exp2(mref - mref): NaN while mref = -inf);
+    // a lane moving away from -inf gets 0, which clears its empty state
+    const float alpha = move ? exp2_fast(w.mref - mxc) : 1.f;
+    w.mref = move ? mxc : w.mref;
+    w.l_run *= alpha;
+#pragma unroll
+    for (int i = 0; i < G::DB; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) w.o[i][r] *= alpha;
+  }
+  const float mu = (w.mref == -INFINITY) ? 0.f : w.mref;
+
+  // ---- P^T as bf16 B operands; fp32 row sums (the LSE needs them unrounded) ----
+  u32x4 pb[2][2];
+  float ls0 = 0.f, ls1 = 0.f;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float p0 = exp2_fast(__builtin_fmaf(s[kb][8 * t + 2 * e], c, -mu));
+        const float p1 = exp2_fast(__builtin_fmaf(s[kb][8 * t + 2 * e + 1], c, -mu));
+        ls0 += p0;
+        ls1 += p1;
+        pb[kb][t][e] = pack_bf16x2(p0, p1);
+      }
+  w.l_run += ls0 + ls1;
+
+  // ---- O^T += V^T P^T; slots (h, 0..3) hold keys 32kb+16t+4h+{0..3}, (h, 4..7) the
+  //      same + 8: one transposed read each ----
+#pragma unroll
+  for (int db = 0; db < G::DB; ++db) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      if (!act[kb]) continue;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const char* vp = sv + w.voff[db] + (32 * kb + 16 * t) * G::kRow;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vp));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vp + 8 * G::kRow));
+        const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
+        const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
+        w.o[db] = mfma32x32x16(u32x4{l2[0], l2[1], h2[0], h2[1]}, pb[kb][t], w.o[db]);
+      }
     }
   }
 }
@@ -137,10 +226,13 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(ATTN_FWD_WAVES_PER_EU, ATTN_FWD_WAVES_PER_EU)))
 void fwd_bf16_kernel(FwdArgs a) {
-  using L = FwdLds<D>;
-  constexpr int KS = D / 16;        // MFMA k-steps over the head dimension
-  constexpr int DB = D / 32;        // 32-wide d blocks of O^T
-  __shared__ __attribute__((aligned(16))) char smem[L::kTotal];
+  using G = Geo<D>;
+  // two stages, each a K tile and a V tile; separate objects so the compiler can tell the
+  // in-flight direct loads into one stage from the reads of the other
+  __shared__ __attribute__((aligned(1024))) char sk0[G::kTile];
+  __shared__ __attribute__((aligned(1024))) char sv0[G::kTile];
+  __shared__ __attribute__((aligned(1024))) char sk1[G::kTile];
+  __shared__ __attribute__((aligned(1024))) char sv1[G::kTile];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -153,14 +245,7 @@ void fwd_bf16_kernel(FwdArgs a) {
   const int id = blockIdx.x;
   const int rank = id / BH;
   const int bh = id - rank * BH;
-  int tile = rank;
-  if (CAUSAL) {
-    // heaviest tiles first; with ZIGZAG the second half of the ranks runs lightest-first,
-    // so the two workgroups that share a CU early on carry complementary amounts of work
-    const int half = (a.ntq + 1) / 2;
-    if (ATTN_FWD_ZIGZAG && rank >= half) tile = rank - half;
-    else tile = a.ntq - 1 - rank;
-  }
+  const int tile = CAUSAL ? (a.ntq - 1 - rank) : rank;
   const int b = bh / a.Hq;
   const int hq = bh - b * a.Hq;
   const int hk = hq / a.group;
@@ -177,158 +262,75 @@ void fwd_bf16_kernel(FwdArgs a) {
   if (CAUSAL) kv_end = min(a.Sk, max(0, q0 + kBM + off));
   const int ntiles = (kv_end + kBN - 1) / kBN;
 
-  // ---- Q^T fragments (B operand), resident for the whole loop ----
-  u32x4 qf[KS];
+  WaveState<D> w;
   {
     const int qi = qw + l32;
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
+    for (int kk = 0; kk < G::KS; ++kk) {
       if (qi < a.Sq)
-        qf[kk] = *reinterpret_cast<const u32x4*>(qbase + (size_t)qi * D + kk * 16 + h * 8);
+        w.qf[kk] = *reinterpret_cast<const u32x4*>(qbase + (size_t)qi * D + kk * 16 + h * 8);
       else
-        qf[kk] = u32x4{0, 0, 0, 0};
+        w.qf[kk] = u32x4{0, 0, 0, 0};
     }
-  }
-
-  f32x16 o[DB];
+    // Consume the Q loads here: otherwise the loop's first use of qf must wait for every
+    // outstanding global load, including the next tile's prefetch.
 #pragma unroll
-  for (int i = 0; i < DB; ++i) o[i] = f32x16{};
-  float m_run = -INFINITY;     // running max of raw scores of this lane's query
-  float l_run = 0.f;           // running sum of exp over this lane's half of the keys
+    for (int kk = 0; kk < G::KS; ++kk) asm volatile("" : "+v"(w.qf[kk]));
+  }
+#pragma unroll
+  for (int i = 0; i < G::DB; ++i) w.o[i] = f32x16{};
+  w.mref = -INFINITY;
+  w.l_run = 0.f;
+  // K operand: row l32 (+32kb), chunk 2kk+h at its permuted slot
+#pragma unroll
+  for (int kk = 0; kk < G::KS; ++kk)
+    w.koff[kk] = l32 * G::kRow + (((2 * kk + h) ^ kswz<D>(l32)) * 16);
+  // V^T operand via transposed reads: source lane (group g, index j) points at key
+  // 4*(g/2) + j/4 (+ the block's first key) and columns 32db + 16*(g%2) + 4*(j%4) .. +3
+  {
+    const int g = lane >> 4, j = lane & 15;
+    const int keyl = 4 * (g >> 1) + (j >> 2);
+    const int small = 2 * (g & 1) + ((j & 3) >> 1);
+#pragma unroll
+    for (int db = 0; db < G::DB; ++db)
+      w.voff[db] = keyl * G::kRow + (((4 * db + small) ^ vswz<D>(keyl)) * 16) + 8 * (j & 1);
+  }
   const float c = a.c;
   const int my_q = qw + l32;
   const int wave_last_key = qw + 31 + off;   // last key any query of this wave may see
 
-  TileRegs<D> tr;
-  if (ntiles > 0) {
-    load_tile<D>(tr, kbase, vbase, 0, a.Sk, tid);
-    store_tile<D>(tr, smem, tid);
-  }
-  __syncthreads();
+  if (ntiles > 0) dma_tile<D>(sk0, sv0, kbase, vbase, 0, a.Sk, wave, lane);
+  wait_dma_and_barrier();
 
-  for (int j = 0; j < ntiles; ++j) {
-    const int kt = j * kBN;
-    char* stage = smem + (j & 1) * L::kStage;
-    const bool more = (j + 1) < ntiles;
-    if (more) load_tile<D>(tr, kbase, vbase, kt + kBN, a.Sk, tid);
-
-    // which 32-key blocks of this tile can be visible to this wave
-    bool act[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-      act[kb] = (kt + 32 * kb < a.Sk) && (!CAUSAL || kt + 32 * kb <= wave_last_key);
-
-    // ---- S^T = K Q^T ----
-    f32x16 s[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = f32x16{};
-      if (act[kb]) {
-        const char* krow = stage + (32 * kb + l32) * L::kPitch + h * 16;
-#pragma unroll
-        for (int kk = 0; kk < KS; ++kk) {
-          const u32x4 kf = *reinterpret_cast<const u32x4*>(krow + kk * 32);
-          s[kb] = mfma32x32x16(kf, qf[kk], s[kb]);
-        }
-      }
-    }
-
-    // ---- mask: causal diagonal, key tail, inactive blocks ----
-    const bool need_mask = (kt + kBN > a.Sk) || (CAUSAL && kt + kBN - 1 > qw + off);
-    if (need_mask) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kt + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
-          bool vis = act[kb] && key < a.Sk;
-          if (CAUSAL) vis = vis && (key <= my_q + off);
-          s[kb][r] = vis ? s[kb][r] : -INFINITY;
-        }
-      }
-    }
-
-    // ---- online softmax (per lane = per query) ----
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) mx = fmax3(mx, s[kb][r], s[kb][r + 1]);
-    mx = fmaxf(mx, wave_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float mc = (m_new == -INFINITY) ? 0.f : m_new * c;
-    const float alpha = exp2_fast(m_run * c - mc);     // m_run = -inf -> 0
-    m_run = m_new;
-
-    float rs = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = exp2_fast(__builtin_fmaf(s[kb][r], c, -mc));
-        s[kb][r] = p;
-        rs += p;
-      }
-    l_run = l_run * alpha + rs;
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
-#pragma unroll
-      for (int i = 0; i < DB; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
-    }
-
-    // ---- P^T as bf16 B operands ----
-    u32x4 pb[2][2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-        pb[kb][t] = u32x4{pack_bf16x2(s[kb][8 * t + 0], s[kb][8 * t + 1]),
-                          pack_bf16x2(s[kb][8 * t + 2], s[kb][8 * t + 3]),
-                          pack_bf16x2(s[kb][8 * t + 4], s[kb][8 * t + 5]),
-                          pack_bf16x2(s[kb][8 * t + 6], s[kb][8 * t + 7])};
-
-    // ---- O^T += V^T P^T ----
-    const char* vt = stage + L::kKBytes;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const int d = 32 * db + l32;
-      const int sw = vt_swz(d);
-      const char* vrow = vt + d * (kBN * 2);
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        if (!act[kb]) continue;
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const int g1 = 8 * kb + 4 * t + h;
-          const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + ((g1 ^ sw) * 8));
-          const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + (((g1 + 2) ^ sw) * 8));
-          const u32x4 vf = {lo[0], lo[1], hi[0], hi[1]};
-          o[db] = mfma32x32x16(vf, pb[kb][t], o[db]);
-        }
-      }
-    }
-
-    if (more) store_tile<D>(tr, smem + ((j + 1) & 1) * L::kStage, tid);
-    __syncthreads();
+  for (int j = 0; j < ntiles; j += 2) {
+    // stage 0 holds tile j; prefetch tile j+1 into stage 1
+    if (j + 1 < ntiles) dma_tile<D>(sk1, sv1, kbase, vbase, (j + 1) * kBN, a.Sk, wave, lane);
+    compute_tile<D, CAUSAL>(w, sk0, sv0, j * kBN, a.Sk, qw, wave_last_key, my_q, off, h, c);
+    wait_dma_and_barrier();
+    if (j + 1 >= ntiles) break;
+    // stage 1 holds tile j+1; prefetch tile j+2 into stage 0
+    if (j + 2 < ntiles) dma_tile<D>(sk0, sv0, kbase, vbase, (j + 2) * kBN, a.Sk, wave, lane);
+    compute_tile<D, CAUSAL>(w, sk1, sv1, (j + 1) * kBN, a.Sk, qw, wave_last_key, my_q, off, h,
+                            c);
+    wait_dma_and_barrier();
   }
 
   // ---- epilogue: normalise, store O (bf16) and LSE (natural log) ----
-  const float l_tot = l_run + wave_xor(l_run, 32);
+  const float l_tot = w.l_run + wave_xor(w.l_run, 32);
   const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
   if (my_q < a.Sq) {
     uint16_t* orow = a.o + ((size_t)(b * a.Hq + hq) * a.Sq + my_q) * D;
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+    for (int db = 0; db < G::DB; ++db)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int d = 32 * db + 8 * g + 4 * h;
-        u32x2 w = {pack_bf16x2(o[db][4 * g + 0] * inv, o[db][4 * g + 1] * inv),
-                   pack_bf16x2(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv)};
-        *reinterpret_cast<u32x2*>(orow + d) = w;
+        u32x2 v = {pack_bf16x2(w.o[db][4 * g + 0] * inv, w.o[db][4 * g + 1] * inv),
+                   pack_bf16x2(w.o[db][4 * g + 2] * inv, w.o[db][4 * g + 3] * inv)};
+        *reinterpret_cast<u32x2*>(orow + d) = v;
       }
     if (a.lse != nullptr && h == 0) {
-      const float lse = (l_tot > 0.f) ? (m_run * c + log2_fast(l_tot)) * kLn2 : -INFINITY;
+      const float lse = (l_tot > 0.f) ? (w.mref + log2_fast(l_tot)) * kLn2 : -INFINITY;
       a.lse[(size_t)(b * a.Hq + hq) * a.Sq + my_q] = lse;
     }
   }

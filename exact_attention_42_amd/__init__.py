@@ -74,7 +74,7 @@ def load_library():
     if _lib is None:
         if not os.path.exists(_LIB_PATH):
             raise ImportError(
-                f"{_LIB_PATH} is missing: build it with `python -m exact_attention_42_amd.build` "
+                f"{_LIB_PATH} is missing: build it with `python exact_attention_42_amd/build.py` "
                 "(there is no fallback implementation)")
         import torch  # noqa: F401  (binds the HIP runtime before libattn.so is loaded)
         lib = ctypes.CDLL(_LIB_PATH)

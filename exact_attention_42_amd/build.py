@@ -1,6 +1,7 @@
 """Build libattn.so (the C-ABI library with the gfx950 kernels) in place with hipcc.
 
-Run ``python -m exact_attention_42_amd.build`` or call :func:`build`. The library is written
+Run ``python exact_attention_42_amd/build.py`` (a plain script: it does not import the package,
+whose import loads the library being rebuilt) or call :func:`build`. The library is written
 next to this file; the sources are ``csrc/*.hip`` and the public header ``include/attn.h``.
 """
 from __future__ import annotations

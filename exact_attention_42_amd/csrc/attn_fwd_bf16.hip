@@ -82,27 +82,51 @@ struct FwdArgs {
   float c;         // scale * log2(e), > 0
 };
 
-// Issue this wave's share of the direct-to-LDS loads of the K/V tile at key kt. Keys past
-// Sk are clamped to Sk-1: they are masked out of the scores, and their (finite) V rows are
-// multiplied by a probability of exactly 0.
+// Direct-to-LDS staging of K/V tiles for one wave. Each lane owns, per direct load, the byte
+// offset within a K (or V) tile of the global chunk it moves: row blk*RPI + lane/CPR, chunk
+// (lane%CPR) ^ permutation(row), so that the chunk lands in its permuted LDS slot.
 template <int D>
-__device__ __forceinline__ void dma_tile(char* sk, char* sv, const uint16_t* kbase,
-                                         const uint16_t* vbase, int kt, int Sk, int wave,
-                                         int lane) {
+struct TileDma {
   using G = Geo<D>;
-  const int pos = lane % G::kCPR;
-  const int rsub = lane / G::kCPR;
+  uint32_t koff[G::kIPW];
+  uint32_t voff[G::kIPW];
+  int wave;   // wave-uniform
+  int lane;
+
+  __device__ __forceinline__ void init(int wave_, int lane_) {
+    wave = wave_;
+    lane = lane_;
+    const int pos = lane % G::kCPR;
+    const int rsub = lane / G::kCPR;
 #pragma unroll
-  for (int i = 0; i < G::kIPW; ++i) {
-    const int blk = wave * G::kIPW + i;
-    const int row = blk * G::kRPI + rsub;
-    const size_t key = (size_t)min(kt + row, Sk - 1);
-    const uint16_t* kp = kbase + key * D + ((pos ^ kswz<D>(row)) * 8);
-    const uint16_t* vp = vbase + key * D + ((pos ^ vswz<D>(row)) * 8);
-    __builtin_amdgcn_global_load_lds(kp, (lds_void*)(sk + blk * 1024), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(vp, (lds_void*)(sv + blk * 1024), 16, 0, 0);
+    for (int i = 0; i < G::kIPW; ++i) {
+      const int row = (wave * G::kIPW + i) * G::kRPI + rsub;
+      koff[i] = row * G::kRow + ((pos ^ kswz<D>(row)) * 16);
+      voff[i] = row * G::kRow + ((pos ^ vswz<D>(row)) * 16);
+    }
   }
-}
+
+  // Issue this wave's share of the loads of the tile at key kt. A tile that runs past Sk
+  // clamps those keys to Sk-1: they are masked out of the scores, and their (finite) V rows
+  // are multiplied by a probability of exactly 0.
+  __device__ __forceinline__ void issue(char* sk, char* sv, const uint16_t* kbase,
+                                        const uint16_t* vbase, int kt, int Sk) const {
+    const char* kt_base = reinterpret_cast<const char*>(kbase + (size_t)kt * D);
+    const char* vt_base = reinterpret_cast<const char*>(vbase + (size_t)kt * D);
+    const int last = Sk - 1 - kt;                 // last valid row of this tile
+    const bool full = last >= kBN - 1;
+#pragma unroll
+    for (int i = 0; i < G::kIPW; ++i) {
+      const int blk = wave * G::kIPW + i;
+      const int row = blk * G::kRPI + lane / G::kCPR;
+      const uint32_t shift = (!full && row > last) ? (uint32_t)((row - last) * G::kRow) : 0u;
+      __builtin_amdgcn_global_load_lds(kt_base + (koff[i] - shift), (lds_void*)(sk + blk * 1024),
+                                       16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vt_base + (voff[i] - shift), (lds_void*)(sv + blk * 1024),
+                                       16, 0, 0);
+    }
+  }
+};
 
 __device__ __forceinline__ void wait_dma_and_barrier() {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -132,20 +156,16 @@ __device__ __forceinline__ void compute_tile(WaveState<D>& w, const char* sk, co
     act[kb] = (kt + 32 * kb < Sk) && (!CAUSAL || kt + 32 * kb <= wave_last_key);
 
   // ---- S^T = K Q^T ----
+  // (computed for every block: a block no query of this wave can see is masked below, and
+  //  skipping it would cost a register copy of every score on all the other tiles)
   f32x16 s[2];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
-    if (act[kb]) {
-      const char* kr = sk + 32 * kb * G::kRow;
-      s[kb] = mfma32x32x16(*reinterpret_cast<const u32x4*>(kr + w.koff[0]), w.qf[0], f32x16{});
+    const char* kr = sk + 32 * kb * G::kRow;
+    s[kb] = mfma32x32x16(*reinterpret_cast<const u32x4*>(kr + w.koff[0]), w.qf[0], f32x16{});
 #pragma unroll
-      for (int kk = 1; kk < G::KS; ++kk)
-        s[kb] = mfma32x32x16(*reinterpret_cast<const u32x4*>(kr + w.koff[kk]), w.qf[kk], s[kb]);
-    } else {
-      // a block no query of this wave can see (it is masked below in any case)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = -INFINITY;
-    }
+    for (int kk = 1; kk < G::KS; ++kk)
+      s[kb] = mfma32x32x16(*reinterpret_cast<const u32x4*>(kr + w.koff[kk]), w.qf[kk], s[kb]);
   }
 
   // ---- mask: causal diagonal, key tail, inactive blocks ----
@@ -173,6 +193,9 @@ __device__ __forceinline__ void compute_tile(WaveState<D>& w, const char* sk, co
   const float mxc = mx * c;                       // -inf stays -inf (c > 0)
   const bool move = mxc > w.mref + kLazy;
   if (__builtin_amdgcn_ballot_w64(move)) {
+    // (the empty asm keeps this a branch: folded into straight-line code, the 64 multiplies
+    //  below would run on every tile)
+    asm volatile("");
     // lanes that keep their reference use 1 (not exp2(mref - mref): NaN while mref = -inf);
     // a lane moving away from -inf gets 0, which clears its empty state
     const float alpha = move ? exp2_fast(w.mref - mxc) : 1.f;
@@ -223,9 +246,7 @@ __device__ __forceinline__ void compute_tile(WaveState<D>& w, const char* sk, co
 }
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(ATTN_FWD_WAVES_PER_EU, ATTN_FWD_WAVES_PER_EU)))
-void fwd_bf16_kernel(FwdArgs a) {
+__device__ __forceinline__ void fwd_bf16_body(const FwdArgs& a) {
   using G = Geo<D>;
   // two stages, each a K tile and a V tile; separate objects so the compiler can tell the
   // in-flight direct loads into one stage from the reads of the other
@@ -236,7 +257,7 @@ void fwd_bf16_kernel(FwdArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = wave_uniform(tid >> 6);
   const int l32 = lane & 31;
   const int h = lane >> 5;
 
@@ -299,17 +320,19 @@ void fwd_bf16_kernel(FwdArgs a) {
   const int my_q = qw + l32;
   const int wave_last_key = qw + 31 + off;   // last key any query of this wave may see
 
-  if (ntiles > 0) dma_tile<D>(sk0, sv0, kbase, vbase, 0, a.Sk, wave, lane);
+  TileDma<D> dma;
+  dma.init(wave, lane);
+  if (ntiles > 0) dma.issue(sk0, sv0, kbase, vbase, 0, a.Sk);
   wait_dma_and_barrier();
 
   for (int j = 0; j < ntiles; j += 2) {
     // stage 0 holds tile j; prefetch tile j+1 into stage 1
-    if (j + 1 < ntiles) dma_tile<D>(sk1, sv1, kbase, vbase, (j + 1) * kBN, a.Sk, wave, lane);
+    if (j + 1 < ntiles) dma.issue(sk1, sv1, kbase, vbase, (j + 1) * kBN, a.Sk);
     compute_tile<D, CAUSAL>(w, sk0, sv0, j * kBN, a.Sk, qw, wave_last_key, my_q, off, h, c);
     wait_dma_and_barrier();
     if (j + 1 >= ntiles) break;
     // stage 1 holds tile j+1; prefetch tile j+2 into stage 0
-    if (j + 2 < ntiles) dma_tile<D>(sk0, sv0, kbase, vbase, (j + 2) * kBN, a.Sk, wave, lane);
+    if (j + 2 < ntiles) dma.issue(sk0, sv0, kbase, vbase, (j + 2) * kBN, a.Sk);
     compute_tile<D, CAUSAL>(w, sk1, sv1, (j + 1) * kBN, a.Sk, qw, wave_last_key, my_q, off, h,
                             c);
     wait_dma_and_barrier();
@@ -336,6 +359,18 @@ void fwd_bf16_kernel(FwdArgs a) {
   }
 }
 
+// The four instances are plain kernels (not a kernel template): their host-side launch stubs
+// then depend only on these signatures.
+#define ATTN_FWD_KERNEL(NAME, D, CAUSAL)                                                  \
+  __global__ __launch_bounds__(kThreads)                                                  \
+  __attribute__((amdgpu_waves_per_eu(ATTN_FWD_WAVES_PER_EU, ATTN_FWD_WAVES_PER_EU)))    \
+  void NAME(FwdArgs a) { fwd_bf16_body<D, CAUSAL>(a); }
+ATTN_FWD_KERNEL(fwd_bf16_d128_causal, 128, true)
+ATTN_FWD_KERNEL(fwd_bf16_d128, 128, false)
+ATTN_FWD_KERNEL(fwd_bf16_d64_causal, 64, true)
+ATTN_FWD_KERNEL(fwd_bf16_d64, 64, false)
+#undef ATTN_FWD_KERNEL
+
 }  // namespace
 
 hipError_t launch_fwd_bf16(const FwdProblem& p, hipStream_t stream) {
@@ -359,11 +394,11 @@ hipError_t launch_fwd_bf16(const FwdProblem& p, hipStream_t stream) {
   if (nwg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   dim3 grid((unsigned)nwg), block(kThreads);
   if (p.D == 128) {
-    if (p.causal) hipLaunchKernelGGL((fwd_bf16_kernel<128, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((fwd_bf16_kernel<128, false>), grid, block, 0, stream, a);
+    if (p.causal) hipLaunchKernelGGL(fwd_bf16_d128_causal, grid, block, 0, stream, a);
+    else hipLaunchKernelGGL(fwd_bf16_d128, grid, block, 0, stream, a);
   } else {
-    if (p.causal) hipLaunchKernelGGL((fwd_bf16_kernel<64, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((fwd_bf16_kernel<64, false>), grid, block, 0, stream, a);
+    if (p.causal) hipLaunchKernelGGL(fwd_bf16_d64_causal, grid, block, 0, stream, a);
+    else hipLaunchKernelGGL(fwd_bf16_d64, grid, block, 0, stream, a);
   }
   return hipGetLastError();
 }

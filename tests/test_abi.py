@@ -125,3 +125,12 @@ def test_one_hip_runtime_in_process():
     """libattn.so must share torch's HIP runtime (same soname); two runtimes in one process
     leave the second one without a device."""
     assert len(A._hip_runtimes_mapped()) <= 1
+
+
+def test_library_defines_every_kernel_launch_stub():
+    """A kernel whose host-side launch stub is missing makes the library fail to load with an
+    undefined symbol; catch that at build time rather than on the GPU."""
+    out = subprocess.run(["nm", "-D", A.library_path()], capture_output=True, text=True,
+                         check=True).stdout
+    undefined = [l for l in out.splitlines() if " U " in l and "device_stub" in l]
+    assert undefined == []

@@ -79,7 +79,9 @@ __device__ int derived_stride(const int32_t* ctx, int B, int lane) {
 
 template <int D>
 struct DecLds {
-  static constexpr int kVPitch = D * 2 + 8;                   // bytes per token row of V
+  // V rows padded by 32 bytes: the 16-byte row writes and the transposing 8-byte column
+  // reads both spread over all 64 banks (D = 128; D = 64 leaves a 2-way conflict on writes)
+  static constexpr int kVPitch = D * 2 + 32;
   static constexpr int kVBytes = kBS * kVPitch;               // one block, one wave
   static constexpr int kVAll = kDecWaves * kVBytes;
   static constexpr int kMerge = kDecWaves * kMaxGroup * D * 4;
@@ -87,22 +89,60 @@ struct DecLds {
   static constexpr int kTotal = kMain + 2 * kDecWaves * kMaxGroup * 4;
 };
 
+// Buffer resource word 3 for raw (untyped) loads on gfx9-family parts.
+constexpr int kRawBufferFlags = 0x00020000;
+
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// The K and V registers of one cache block for one wave.
 template <int D>
-__global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecArgs a) {
+struct DecFrag {
+  static constexpr int KS = D / 32;                 // K: 16x16x32 A-operand k-steps
+  static constexpr int VLD = kBS * D * 2 / 16 / 64;  // V: 16-byte loads per lane
+  u32x4 k[KS];
+  u32x4 v[VLD];
+};
+
+// Loads one block through buffer resources whose size is the block's live bytes: rows past
+// the context, and whole blocks whose table entry is invalid (size 0), come back as zeros
+// without touching memory. Zero V rows keep 0 * stale-NaN out of the matrix core.
+template <int D>
+__device__ __forceinline__ void dec_load(DecFrag<D>& f, const uint16_t* kbase,
+                                         const uint16_t* vbase, int bytes, int koff, int voff) {
+  const __amdgpu_buffer_rsrc_t rk =
+      __builtin_amdgcn_make_buffer_rsrc((void*)kbase, 0, bytes, kRawBufferFlags);
+  const __amdgpu_buffer_rsrc_t rv =
+      __builtin_amdgcn_make_buffer_rsrc((void*)vbase, 0, bytes, kRawBufferFlags);
+#pragma unroll
+  for (int kk = 0; kk < DecFrag<D>::KS; ++kk)
+    f.k[kk] = __builtin_amdgcn_raw_buffer_load_b128(rk, koff + kk * 64, 0, 0);
+#pragma unroll
+  for (int i = 0; i < DecFrag<D>::VLD; ++i)
+    f.v[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, voff + i * 1024, 0, 0);
+}
+
+#ifndef ATTN_DEC_WAVES_PER_EU
+#define ATTN_DEC_WAVES_PER_EU 3
+#endif
+
+template <int D>
+__global__ __launch_bounds__(kDecThreads)
+__attribute__((amdgpu_waves_per_eu(ATTN_DEC_WAVES_PER_EU))) void decode_split_kernel(DecArgs a) {
   using L = DecLds<D>;
-  constexpr int KS = D / 32;        // 16x16x32 k-steps for q.K
+  using F = DecFrag<D>;
+  constexpr int KS = F::KS;
   constexpr int DT = D / 16;        // 16-row d tiles of O^T
   constexpr int VCH = D / 8;        // 16-byte chunks per token row
-  constexpr int VLD = kBS * VCH / 64;  // 16-byte V loads per lane per block
   __shared__ __attribute__((aligned(16))) char smem[L::kTotal];
 
   const int sp = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = wave_uniform(tid >> 6);   // scalar: the block addresses below are per wave
   const int ctx = a.ctx[b];
+  const int stride = a.stride > 0 ? a.stride : derived_stride(a.ctx, a.B, lane);
   const int nblk = seq_blocks(ctx, a.stride);
   const int ns = num_splits(nblk, a.max_splits);
   if (sp >= ns) return;                       // uniform for the whole workgroup
-  const int stride = a.stride > 0 ? a.stride : derived_stride(a.ctx, a.B, lane);
   const int bps = (nblk + ns - 1) / ns;
   const int n0 = sp * bps;
   const int n1 = min(nblk, n0 + bps);
@@ -129,69 +169,94 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecArgs a) {
   const float c = a.c;
   char* vl = smem + wave * L::kVBytes;
   const int32_t* trow = a.table + (size_t)b * stride;
+  const size_t tile_elems = (size_t)kBS * D;
+  const uint16_t* kc = a.kc + (size_t)hk * tile_elems;
+  const uint16_t* vc = a.vc + (size_t)hk * tile_elems;
+  const size_t phys_elems = (size_t)a.Hkv * tile_elems;
+  const int koff = r16 * 2 * D + grp * 16;   // K: row r16, 8 columns of slot group grp
+  const int voff = lane * 16;                // V: contiguous 1 KiB per load
+  // the transposing read: lane (grp, r16) addresses key 4*grp + r16/4, columns 4*(r16%4)..+3
+  const char* vtr = vl + (4 * grp + (r16 >> 2)) * L::kVPitch + (r16 & 3) * 8;
 
-  for (int n = n0 + wave; n < n1; n += kDecWaves) {
-    const int phys = trow[n];
-    if (a.num_blocks > 0 && (phys < 0 || phys >= a.num_blocks)) continue;   // invalid entry
-    const size_t tile = ((size_t)phys * a.Hkv + hk) * kBS * D;
-    const uint16_t* kt = a.kc + tile;
-    const uint16_t* vt = a.vc + tile;
-    u32x4 kf[KS];
+  // this wave's blocks are first + 4j, j < cnt; table entries are fetched 64 at a time
+  const int first = n0 + wave;
+  const int cnt = first < n1 ? (n1 - first + 3) / 4 : 0;
+  for (int c0 = 0; c0 < cnt; c0 += 64) {
+    const int cc = min(64, cnt - c0);
+    const int tv = lane < cc ? trow[first + 4 * (c0 + lane)] : 0;
+
+    // live bytes of block j of this chunk (0 past the chunk or for an invalid entry)
+    auto block_src = [&](int j, const uint16_t*& kb, const uint16_t*& vb) -> int {
+      const int phys = __builtin_amdgcn_readlane(tv, j & 63);
+      const int n = first + 4 * (c0 + j);
+      const bool ok = j < cc && (a.num_blocks <= 0 || (phys >= 0 && phys < a.num_blocks));
+      const size_t off = ok ? (size_t)phys * phys_elems : 0;
+      kb = kc + off;
+      vb = vc + off;
+      return ok ? min(kBS, ctx - n * kBS) * 2 * D : 0;
+    };
+
+    auto process = [&](const F& f, int j) {
+      const uint16_t *kb, *vb;
+      const int live = block_src(j, kb, vb) / (2 * D);   // live tokens of this block
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk)
-      kf[kk] = *reinterpret_cast<const u32x4*>(kt + r16 * D + kk * 32 + grp * 8);
-    u32x4 vr[VLD];
+      for (int i = 0; i < F::VLD; ++i) {
+        const int ci = lane + 64 * i;
+        *reinterpret_cast<u32x4*>(vl + (ci / VCH) * L::kVPitch + (ci % VCH) * 16) = f.v[i];
+      }
+      f32x4 s = f32x4{};
 #pragma unroll
-    for (int i = 0; i < VLD; ++i) {
-      const int ci = lane + 64 * i;
-      vr[i] = *reinterpret_cast<const u32x4*>(vt + (ci / VCH) * D + (ci % VCH) * 8);
+      for (int kk = 0; kk < KS; ++kk) s = mfma16x16x32(f.k[kk], qf[kk], s);
+
+      // lane holds tokens 4*grp + j of this block for head r16
+#pragma unroll
+      for (int t = 0; t < 4; ++t) s[t] = (4 * grp + t < live) ? s[t] : -INFINITY;
+      float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+      mx = fmaxf(mx, wave_xor(mx, 16));
+      mx = fmaxf(mx, wave_xor(mx, 32));
+      const float m_new = fmaxf(m_run, mx);
+      const float mc = (m_new == -INFINITY) ? 0.f : m_new * c;
+      const float alpha = exp2_fast(m_run * c - mc);
+      m_run = m_new;
+      float p[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) p[t] = exp2_fast(__builtin_fmaf(s[t], c, -mc));
+      l_run = l_run * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+#pragma unroll
+      for (int i = 0; i < DT; ++i) acc[i] *= alpha;
+      const u32x2 pb = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
+
+      wave_lds_fence();
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const i16x4 vt = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vtr + 32 * dt));
+        acc[dt] = mfma16x16x16(__builtin_bit_cast(u32x2, vt), pb, acc[dt]);
+      }
+      wave_lds_fence();
+    };
+
+    // two register sets: block j+1 is in flight while block j is processed
+    F fa, fb;
+    {
+      const uint16_t *kb, *vb;
+      const int bytes = block_src(0, kb, vb);
+      dec_load<D>(fa, kb, vb, bytes, koff, voff);
     }
-    // slots past the end of the context hold stale data (possibly NaN): the matrix core
-    // would multiply them by p = 0 and still produce NaN, so they are staged as zeros
-#pragma unroll
-    for (int i = 0; i < VLD; ++i) {
-      const int ci = lane + 64 * i;
-      const bool live = n * kBS + ci / VCH < ctx;
-      char* dst = vl + (ci / VCH) * L::kVPitch + (ci % VCH) * 16;
-      *reinterpret_cast<u32x2*>(dst) = live ? u32x2{vr[i][0], vr[i][1]} : u32x2{0, 0};
-      *reinterpret_cast<u32x2*>(dst + 8) = live ? u32x2{vr[i][2], vr[i][3]} : u32x2{0, 0};
+    for (int j = 0; j < cc; j += 2) {
+      {
+        const uint16_t *kb, *vb;
+        const int bytes = block_src(j + 1, kb, vb);
+        dec_load<D>(fb, kb, vb, bytes, koff, voff);
+      }
+      process(fa, j);
+      if (j + 1 >= cc) break;
+      {
+        const uint16_t *kb, *vb;
+        const int bytes = block_src(j + 2, kb, vb);
+        dec_load<D>(fa, kb, vb, bytes, koff, voff);
+      }
+      process(fb, j + 1);
     }
-
-    f32x4 s = f32x4{};
-#pragma unroll
-    for (int kk = 0; kk < KS; ++kk) s = mfma16x16x32(kf[kk], qf[kk], s);
-
-    // lane holds tokens 4*grp + j of this block for head r16
-    const int tok0 = n * kBS + 4 * grp;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) s[j] = (tok0 + j < ctx) ? s[j] : -INFINITY;
-    float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-    mx = fmaxf(mx, wave_xor(mx, 16));
-    mx = fmaxf(mx, wave_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float mc = (m_new == -INFINITY) ? 0.f : m_new * c;
-    const float alpha = exp2_fast(m_run * c - mc);
-    m_run = m_new;
-    float p[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) p[j] = exp2_fast(__builtin_fmaf(s[j], c, -mc));
-    l_run = l_run * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
-#pragma unroll
-    for (int i = 0; i < DT; ++i) acc[i] *= alpha;
-    const u32x2 pb = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
-
-    wave_lds_fence();
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const char* col = vl + (4 * grp) * L::kVPitch + (16 * dt + r16) * 2;
-      const uint32_t t0 = *reinterpret_cast<const uint16_t*>(col);
-      const uint32_t t1 = *reinterpret_cast<const uint16_t*>(col + L::kVPitch);
-      const uint32_t t2 = *reinterpret_cast<const uint16_t*>(col + 2 * L::kVPitch);
-      const uint32_t t3 = *reinterpret_cast<const uint16_t*>(col + 3 * L::kVPitch);
-      const u32x2 va = {t0 | (t1 << 16), t2 | (t3 << 16)};
-      acc[dt] = mfma16x16x16(va, pb, acc[dt]);
-    }
-    wave_lds_fence();
   }
 
   // ---- merge the four wave states of this split ----

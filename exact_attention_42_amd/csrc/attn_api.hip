@@ -76,6 +76,10 @@ int run_fwd(bool f32, const void* q, const void* k, const void* v, void* o, floa
             int Hq, int Hkv, int Sq, int Sk, int D, int causal, float scale, void* stream) {
   bool empty;
   if (int rc = check_fwd(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, &empty)) return rc;
+  // the bf16 kernel addresses one head's K (and V) through a buffer resource with 32-bit
+  // signed offsets
+  if (!f32 && (long long)Sk * D * 2 > 0x7fffffffLL)
+    return fail(ATTN_ERR_SHAPE, "Sk=%d too long for D=%d: Sk*D*2 must stay below 2^31", Sk, D);
   if (empty) return ok();
   attn::FwdProblem p{q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, causal ? 1 : 0, scale};
   hipError_t e = f32 ? attn::launch_fwd_f32(p, static_cast<hipStream_t>(stream))

@@ -82,20 +82,30 @@ struct FwdArgs {
   float c;         // scale * log2(e), > 0
 };
 
+// Buffer resource word 3 for raw (untyped) loads on gfx9-family parts.
+constexpr int kRawBufferFlags = 0x00020000;
+
 // Direct-to-LDS staging of K/V tiles for one wave. Each lane owns, per direct load, the byte
 // offset within a K (or V) tile of the global chunk it moves: row blk*RPI + lane/CPR, chunk
-// (lane%CPR) ^ permutation(row), so that the chunk lands in its permuted LDS slot.
+// (lane%CPR) ^ permutation(row), so that the chunk lands in its permuted LDS slot. The loads
+// go through buffer resources over this head's K and V, so a tile is addressed by a scalar
+// offset and the per-lane offsets stay fixed: no vector ALU work per load.
 template <int D>
 struct TileDma {
   using G = Geo<D>;
   uint32_t koff[G::kIPW];
   uint32_t voff[G::kIPW];
+  __amdgpu_buffer_rsrc_t rk, rv;
   int wave;   // wave-uniform
   int lane;
 
-  __device__ __forceinline__ void init(int wave_, int lane_) {
+  __device__ __forceinline__ void init(int wave_, int lane_, const uint16_t* kbase,
+                                       const uint16_t* vbase, int Sk) {
     wave = wave_;
     lane = lane_;
+    const int bytes = Sk * G::kRow;   // the launcher keeps this below 2^31
+    rk = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, 0, bytes, kRawBufferFlags);
+    rv = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, 0, bytes, kRawBufferFlags);
     const int pos = lane % G::kCPR;
     const int rsub = lane / G::kCPR;
 #pragma unroll
@@ -109,21 +119,29 @@ struct TileDma {
   // Issue this wave's share of the loads of the tile at key kt. A tile that runs past Sk
   // clamps those keys to Sk-1: they are masked out of the scores, and their (finite) V rows
   // are multiplied by a probability of exactly 0.
-  __device__ __forceinline__ void issue(char* sk, char* sv, const uint16_t* kbase,
-                                        const uint16_t* vbase, int kt, int Sk) const {
-    const char* kt_base = reinterpret_cast<const char*>(kbase + (size_t)kt * D);
-    const char* vt_base = reinterpret_cast<const char*>(vbase + (size_t)kt * D);
+  __device__ __forceinline__ void issue(char* sk, char* sv, int kt, int Sk) const {
+    const int tile_off = kt * G::kRow;
     const int last = Sk - 1 - kt;                 // last valid row of this tile
-    const bool full = last >= kBN - 1;
+    if (last >= kBN - 1) {
 #pragma unroll
-    for (int i = 0; i < G::kIPW; ++i) {
-      const int blk = wave * G::kIPW + i;
-      const int row = blk * G::kRPI + lane / G::kCPR;
-      const uint32_t shift = (!full && row > last) ? (uint32_t)((row - last) * G::kRow) : 0u;
-      __builtin_amdgcn_global_load_lds(kt_base + (koff[i] - shift), (lds_void*)(sk + blk * 1024),
-                                       16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vt_base + (voff[i] - shift), (lds_void*)(sv + blk * 1024),
-                                       16, 0, 0);
+      for (int i = 0; i < G::kIPW; ++i) {
+        const int blk = wave * G::kIPW + i;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(sk + blk * 1024), 16, koff[i],
+                                                 tile_off, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(sv + blk * 1024), 16, voff[i],
+                                                 tile_off, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < G::kIPW; ++i) {
+        const int blk = wave * G::kIPW + i;
+        const int row = blk * G::kRPI + lane / G::kCPR;
+        const uint32_t shift = row > last ? (uint32_t)((row - last) * G::kRow) : 0u;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(sk + blk * 1024), 16,
+                                                 koff[i] - shift, tile_off, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(sv + blk * 1024), 16,
+                                                 voff[i] - shift, tile_off, 0, 0);
+      }
     }
   }
 };
@@ -144,6 +162,43 @@ struct WaveState {
   int voff[G::DB];          // per-lane V^T transposed-read offsets within a tile
 };
 
+// max / sum of x over lanes l and l ^ 32. v_permlane32_swap returns the low half of x in
+// both halves of one register and the high half in both halves of the other, so the pair
+// (l, l ^ 32) meets in every lane with no LDS round trip.
+__device__ __forceinline__ float xor32_max(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+}
+
+// O^T += V^T P^T for the first NKB 32-key blocks of the tile. Slots (h, 0..3) of P^T hold
+// keys 32kb+16t+4h+{0..3} and slots (h, 4..7) the same + 8: one transposed read each.
+template <int D, int NKB>
+__device__ __forceinline__ void pv_blocks(WaveState<D>& w, const char* sv,
+                                          const u32x4 (&pb)[2][2]) {
+  using G = Geo<D>;
+#pragma unroll
+  for (int db = 0; db < G::DB; ++db) {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const char* vp = sv + w.voff[db] + (32 * kb + 16 * t) * G::kRow;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vp));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vp + 8 * G::kRow));
+        const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
+        const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
+        w.o[db] = mfma32x32x16(u32x4{l2[0], l2[1], h2[0], h2[1]}, pb[kb][t], w.o[db]);
+      }
+    }
+  }
+}
+
 // One K/V tile: S^T = K Q^T, mask, online softmax, O^T += V^T P^T.
 template <int D, bool CAUSAL>
 __device__ __forceinline__ void compute_tile(WaveState<D>& w, const char* sk, const char* sv,
@@ -158,15 +213,19 @@ __device__ __forceinline__ void compute_tile(WaveState<D>& w, const char* sk, co
   // ---- S^T = K Q^T ----
   // (computed for every block: a block no query of this wave can see is masked below, and
   //  skipping it would cost a register copy of every score on all the other tiles)
+  u32x4 kf[2][G::KS];
+#pragma unroll
+  for (int kk = 0; kk < G::KS; ++kk)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+      kf[kb][kk] = *reinterpret_cast<const u32x4*>(sk + 32 * kb * G::kRow + w.koff[kk]);
   f32x16 s[2];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    const char* kr = sk + 32 * kb * G::kRow;
-    s[kb] = mfma32x32x16(*reinterpret_cast<const u32x4*>(kr + w.koff[0]), w.qf[0], f32x16{});
+  for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32x32x16(kf[kb][0], w.qf[0], f32x16{});
 #pragma unroll
-    for (int kk = 1; kk < G::KS; ++kk)
-      s[kb] = mfma32x32x16(*reinterpret_cast<const u32x4*>(kr + w.koff[kk]), w.qf[kk], s[kb]);
-  }
+  for (int kk = 1; kk < G::KS; ++kk)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32x32x16(kf[kb][kk], w.qf[kk], s[kb]);
 
   // ---- mask: causal diagonal, key tail, inactive blocks ----
   const bool need_mask = (kt + kBN > Sk) || (CAUSAL && kt + kBN - 1 > qw + off);
@@ -189,7 +248,7 @@ __device__ __forceinline__ void compute_tile(WaveState<D>& w, const char* sk, co
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int r = 0; r < 16; r += 2) mx = fmax3(mx, s[kb][r], s[kb][r + 1]);
-  mx = fmaxf(mx, wave_xor(mx, 32));
+  mx = xor32_max(mx);
   const float mxc = mx * c;                       // -inf stays -inf (c > 0)
   const bool move = mxc > w.mref + kLazy;
   if (__builtin_amdgcn_ballot_w64(move)) {
@@ -210,7 +269,7 @@ __device__ __forceinline__ void compute_tile(WaveState<D>& w, const char* sk, co
 
   // ---- P^T as bf16 B operands; fp32 row sums (the LSE needs them unrounded) ----
   u32x4 pb[2][2];
-  float ls0 = 0.f, ls1 = 0.f;
+  float ls[2];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -219,30 +278,20 @@ __device__ __forceinline__ void compute_tile(WaveState<D>& w, const char* sk, co
       for (int e = 0; e < 4; ++e) {
         const float p0 = exp2_fast(__builtin_fmaf(s[kb][8 * t + 2 * e], c, -mu));
         const float p1 = exp2_fast(__builtin_fmaf(s[kb][8 * t + 2 * e + 1], c, -mu));
-        ls0 += p0;
-        ls1 += p1;
+        if (kb == 0 && t == 0 && e == 0) {
+          ls[0] = p0;
+          ls[1] = p1;
+        } else {
+          ls[0] += p0;
+          ls[1] += p1;
+        }
         pb[kb][t][e] = pack_bf16x2(p0, p1);
       }
-  w.l_run += ls0 + ls1;
+  w.l_run += ls[0] + ls[1];
 
-  // ---- O^T += V^T P^T; slots (h, 0..3) hold keys 32kb+16t+4h+{0..3}, (h, 4..7) the
-  //      same + 8: one transposed read each ----
-#pragma unroll
-  for (int db = 0; db < G::DB; ++db) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      if (!act[kb]) continue;
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const char* vp = sv + w.voff[db] + (32 * kb + 16 * t) * G::kRow;
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vp));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vp + 8 * G::kRow));
-        const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
-        const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
-        w.o[db] = mfma32x32x16(u32x4{l2[0], l2[1], h2[0], h2[1]}, pb[kb][t], w.o[db]);
-      }
-    }
-  }
+  // ---- O^T += V^T P^T over the active 32-key blocks (a uniform choice per tile) ----
+  if (act[1]) pv_blocks<D, 2>(w, sv, pb);
+  else if (act[0]) pv_blocks<D, 1>(w, sv, pb);
 }
 
 template <int D, bool CAUSAL>
@@ -321,25 +370,25 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs& a) {
   const int wave_last_key = qw + 31 + off;   // last key any query of this wave may see
 
   TileDma<D> dma;
-  dma.init(wave, lane);
-  if (ntiles > 0) dma.issue(sk0, sv0, kbase, vbase, 0, a.Sk);
+  dma.init(wave, lane, kbase, vbase, a.Sk);
+  if (ntiles > 0) dma.issue(sk0, sv0, 0, a.Sk);
   wait_dma_and_barrier();
 
   for (int j = 0; j < ntiles; j += 2) {
     // stage 0 holds tile j; prefetch tile j+1 into stage 1
-    if (j + 1 < ntiles) dma.issue(sk1, sv1, kbase, vbase, (j + 1) * kBN, a.Sk);
+    if (j + 1 < ntiles) dma.issue(sk1, sv1, (j + 1) * kBN, a.Sk);
     compute_tile<D, CAUSAL>(w, sk0, sv0, j * kBN, a.Sk, qw, wave_last_key, my_q, off, h, c);
     wait_dma_and_barrier();
     if (j + 1 >= ntiles) break;
     // stage 1 holds tile j+1; prefetch tile j+2 into stage 0
-    if (j + 2 < ntiles) dma.issue(sk0, sv0, kbase, vbase, (j + 2) * kBN, a.Sk);
+    if (j + 2 < ntiles) dma.issue(sk0, sv0, (j + 2) * kBN, a.Sk);
     compute_tile<D, CAUSAL>(w, sk1, sv1, (j + 1) * kBN, a.Sk, qw, wave_last_key, my_q, off, h,
                             c);
     wait_dma_and_barrier();
   }
 
   // ---- epilogue: normalise, store O (bf16) and LSE (natural log) ----
-  const float l_tot = w.l_run + wave_xor(w.l_run, 32);
+  const float l_tot = xor32_sum(w.l_run);
   const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
   if (my_q < a.Sq) {
     uint16_t* orow = a.o + ((size_t)(b * a.Hq + hq) * a.Sq + my_q) * D;

@@ -56,7 +56,8 @@ enum attn_status {
 };
 
 /* Prefill / full-sequence forward, bfloat16 q, k, v, o (float32 lse).
- * lse may be NULL (not written). Layouts and semantics as above. D in {64, 128}. */
+ * lse may be NULL (not written). Layouts and semantics as above. D in {64, 128}.
+ * One head's K (and V) must be under 2 GiB: Sk * D * 2 < 2^31, else ATTN_ERR_SHAPE. */
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              int B, int Hq, int Hkv, int Sq, int Sk, int D,
              int causal, float scale, void* stream);

@@ -66,6 +66,13 @@ def test_fwd_rejects(kw, code, f32):
     assert A.attn_last_error() != ""
 
 
+def test_fwd_bf16_rejects_a_head_over_2gib():
+    # one head's K must fit the kernel's 32-bit buffer offsets; the f32 path has no such limit
+    assert fwd(Sk=1 << 23, D=128) == SHAPE
+    assert "2^31" in A.attn_last_error()
+    assert fwd(Sk=1 << 24, D=64) == SHAPE
+
+
 @pytest.mark.parametrize("kw", [dict(B=0), dict(Sq=0), dict(B=0, q=0, k=0, v=0, o=0),
                                 dict(Sq=0, q=0, o=0)])
 def test_fwd_empty_problem_is_a_no_op(kw):

@@ -4,23 +4,39 @@
 // Integration: tile Q, K, V on chip; scores, softmax and the weighted sum in a single pass;
 // online softmax; O(N) memory).
 //
-// Work mapping: one workgroup of 4 waves per (batch, query head, 128-query tile); each wave
-// owns 32 queries. Query head h reads KV head h / (Hq / Hkv) (grouped-query attention).
-// The kernel works on the transposed problem so that the softmax runs inside each lane:
+// Queries are cut into 128-row tiles and each wave owns 32 rows of a tile. Query head h reads
+// KV head h / (Hq / Hkv) (grouped-query attention). Two work mappings share the tile code:
+//
+//  * Tile kernel: a workgroup of 4 waves per (batch, query head, tile), two workgroups per CU.
+//    With a causal mask tiles are issued heaviest first, which balances the CUs when there are
+//    many more workgroups than CU slots (long sequences).
+//  * Pair kernel (causal launches with few tiles per head, where one round of workgroups would
+//    be set by its heaviest tile): a workgroup of 8 waves, one per CU, takes the pair of tiles
+//    (p, T-1-p), a light one that sees few keys and a heavy one that sees many, and splits it
+//    so that all 8 waves do the same number of K/V tiles: waves 4..7 ("H") take the heavy
+//    tile's rows over the first x key tiles; waves 0..3 ("L") take the light tile's rows over
+//    the same key tiles (loaded once for both), then the heavy tile's rows over the remaining
+//    key tiles, last tile first. At the end each L wave hands its partial softmax state to the
+//    H wave with the same rows through LDS, where the two are merged with the online-softmax
+//    rescaling. Every workgroup then does about the same work. Work items of one KV head are
+//    placed on one XCD so they share its L2, and the L waves raise their issue priority around
+//    their matrix-core work so the two waves of a SIMD drift out of step.
+//
+// Each wave works on the transposed problem so that the softmax runs inside each lane:
 //   S^T[key][q] = K[key][:] . Q[q][:]        (MFMA 32x32x16: A = K from LDS, B = Q^T in VGPRs)
 //   O^T[d][q]  += V^T[d][key] P^T[key][q]    (MFMA 32x32x16: A = V^T from LDS, B = P^T in VGPRs)
-// With this orientation a lane's accumulator column is one query, so the running max and
-// sum are per lane: a row max needs one exchange with lane l^32, and P^T leaves the first
-// product's accumulators in exactly the B-operand layout of the second (no LDS round trip).
+// A lane's accumulator column is one query, so the running max and sum are per lane: a row max
+// needs one exchange with lane l^32 (v_permlane32_swap), and P^T leaves the first product's
+// accumulators in exactly the B-operand layout of the second (no LDS round trip).
 //
 // K/V staging: tiles of 64 keys go from global memory straight into LDS with direct-to-LDS
-// loads (global_load_lds_dwordx4: each lane's 16 bytes land at base + 16*lane), double
-// buffered, so no registers or ALU work are spent on staging. Rows are stored unpadded with
-// their 16-byte chunks XOR-permuted; each lane fetches the global chunk that belongs in its
-// LDS slot. The K permutation (chunk ^ row%16) makes the row-per-lane ds_read_b128 operand
-// reads conflict-free; V stays row-major and its V^T operand comes from the transposing read
-// ds_read_b64_tr_b16 (each group of 16 lanes turns 4 keys x 16 columns into 16 lanes x 4
-// keys), with the V permutation (chunk ^ 4*(row%4)) spreading those reads over all banks.
+// buffer loads (each lane's 16 bytes land at base + 16*lane), double buffered (the pair kernel
+// keeps a second stream for the heavy tail). Rows are stored unpadded with their 16-byte chunks
+// XOR-permuted; each lane fetches the global chunk that belongs in its LDS slot. The K
+// permutation (chunk ^ row%16) makes the row-per-lane ds_read_b128 operand reads conflict-free;
+// V stays row-major and its V^T operand comes from the transposing read ds_read_b64_tr_b16
+// (each group of 16 lanes turns 4 keys x 16 columns into 16 lanes x 4 keys), with the V
+// permutation (chunk ^ 4*(row%4)) spreading those reads over all banks.
 //
 // Softmax: base 2 with scale*log2(e) folded into one FMA per score. The running reference
 // max is only moved when a row's max exceeds it by more than 2^8 (lazy rescale): until then
@@ -28,8 +44,8 @@
 // rounding, while the O accumulators are rescaled only a handful of times per row.
 //
 // Causal masking is bottom-right aligned (key j visible to query i iff j <= i + Sk - Sq);
-// tiles wholly above the diagonal are never loaded, and 32-key blocks above a wave's
-// diagonal are skipped by that wave. Tiles are issued heaviest first.
+// tiles wholly above a wave's diagonal are skipped by that wave, and tiles no row of the
+// workgroup sees are never loaded.
 #include "cdna4.hpp"
 #include "kernels.hpp"
 
@@ -38,25 +54,22 @@ namespace {
 
 using namespace cdna4;
 
-#ifndef ATTN_FWD_WAVES_PER_EU
-#define ATTN_FWD_WAVES_PER_EU 2
-#endif
-
-constexpr int kBM = 128;
-constexpr int kBN = 64;
-constexpr int kThreads = 256;
+constexpr int kBM = 128;           // query rows per tile
+constexpr int kBN = 64;            // keys per K/V tile
 constexpr float kLazy = 8.0f;      // log2 of the largest probability allowed before rescaling
+// Pair kernel is used for causal launches with at most this many tiles per head.
+constexpr int kPairMaxTiles = 64;
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-template <int D>
+template <int D, int WAVES>
 struct Geo {
   static constexpr int kRow = 2 * D;              // bytes per K or V row in LDS
   static constexpr int kTile = kBN * kRow;        // one K or V tile
   static constexpr int kCPR = D / 8;              // 16-byte chunks per row
   static constexpr int kRPI = 1024 / kRow;        // rows per 1 KiB direct load
-  static constexpr int kIPW = kTile / 1024 / 4;   // direct loads per wave, per tensor, per tile
+  static constexpr int kIPW = kTile / 1024 / WAVES;  // direct loads per wave, tensor and tile
   static constexpr int KS = D / 16;               // MFMA k-steps over the head dimension
   static constexpr int DB = D / 32;               // 32-wide d blocks of O^T
 };
@@ -78,21 +91,22 @@ struct FwdArgs {
   int B, Hq, Hkv, Sq, Sk;
   int group;       // Hq / Hkv
   int ntq;         // number of 128-query tiles
-  int causal;
+  int npairs;      // pair kernel: work items per (batch, query head)
+  int nitems;      // pair kernel: B * Hq * npairs
   float c;         // scale * log2(e), > 0
 };
 
 // Buffer resource word 3 for raw (untyped) loads on gfx9-family parts.
 constexpr int kRawBufferFlags = 0x00020000;
 
-// Direct-to-LDS staging of K/V tiles for one wave. Each lane owns, per direct load, the byte
-// offset within a K (or V) tile of the global chunk it moves: row blk*RPI + lane/CPR, chunk
-// (lane%CPR) ^ permutation(row), so that the chunk lands in its permuted LDS slot. The loads
-// go through buffer resources over this head's K and V, so a tile is addressed by a scalar
-// offset and the per-lane offsets stay fixed: no vector ALU work per load.
-template <int D>
+// Direct-to-LDS staging of K/V tiles; each wave issues its share of a tile. Each lane owns,
+// per direct load, the byte offset within a K (or V) tile of the global chunk it moves: row
+// blk*RPI + lane/CPR, chunk (lane%CPR) ^ permutation(row), so that the chunk lands in its
+// permuted LDS slot. The loads go through buffer resources over this head's K and V, so a
+// tile is addressed by a scalar offset and the per-lane offsets stay fixed.
+template <int D, int WAVES>
 struct TileDma {
-  using G = Geo<D>;
+  using G = Geo<D, WAVES>;
   uint32_t koff[G::kIPW];
   uint32_t voff[G::kIPW];
   __amdgpu_buffer_rsrc_t rk, rv;
@@ -103,7 +117,7 @@ struct TileDma {
                                        const uint16_t* vbase, int Sk) {
     wave = wave_;
     lane = lane_;
-    const int bytes = Sk * G::kRow;   // the launcher keeps this below 2^31
+    const int bytes = Sk * G::kRow;   // the C ABI keeps this below 2^31
     rk = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, 0, bytes, kRawBufferFlags);
     rv = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, 0, bytes, kRawBufferFlags);
     const int pos = lane % G::kCPR;
@@ -132,6 +146,9 @@ struct TileDma {
                                                  tile_off, 0, 0);
       }
     } else {
+      // (the empty asm keeps this a branch: folded into straight-line code, the clamping
+      //  below would run on every tile)
+      asm volatile("");
 #pragma unroll
       for (int i = 0; i < G::kIPW; ++i) {
         const int blk = wave * G::kIPW + i;
@@ -153,7 +170,7 @@ __device__ __forceinline__ void wait_dma_and_barrier() {
 
 template <int D>
 struct WaveState {
-  using G = Geo<D>;
+  using G = Geo<D, 4>;
   u32x4 qf[G::KS];          // Q^T fragments (B operand)
   f32x16 o[G::DB];          // O^T accumulators
   float mref;               // reference max (scaled, base 2) of this lane's query
@@ -181,7 +198,7 @@ __device__ __forceinline__ float xor32_sum(float x) {
 template <int D, int NKB>
 __device__ __forceinline__ void pv_blocks(WaveState<D>& w, const char* sv,
                                           const u32x4 (&pb)[2][2]) {
-  using G = Geo<D>;
+  using G = Geo<D, 4>;
 #pragma unroll
   for (int db = 0; db < G::DB; ++db) {
 #pragma unroll
@@ -203,13 +220,14 @@ __device__ __forceinline__ void pv_blocks(WaveState<D>& w, const char* sv,
 template <int D, bool CAUSAL>
 __device__ __forceinline__ void compute_tile(WaveState<D>& w, const char* sk, const char* sv,
                                              int kt, int Sk, int qw, int wave_last_key,
-                                             int my_q, int off, int h, float c) {
-  using G = Geo<D>;
+                                             int my_q, int off, int h, float c, bool lead) {
+  using G = Geo<D, 4>;
   bool act[2];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
     act[kb] = (kt + 32 * kb < Sk) && (!CAUSAL || kt + 32 * kb <= wave_last_key);
 
+  if (lead) __builtin_amdgcn_s_setprio(2);
   // ---- S^T = K Q^T ----
   // (computed for every block: a block no query of this wave can see is masked below, and
   //  skipping it would cost a register copy of every score on all the other tiles)
@@ -227,6 +245,7 @@ __device__ __forceinline__ void compute_tile(WaveState<D>& w, const char* sk, co
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32x32x16(kf[kb][kk], w.qf[kk], s[kb]);
 
+  if (lead) __builtin_amdgcn_s_setprio(0);
   // ---- mask: causal diagonal, key tail, inactive blocks ----
   const bool need_mask = (kt + kBN > Sk) || (CAUSAL && kt + kBN - 1 > qw + off);
   if (need_mask) {
@@ -290,13 +309,24 @@ __device__ __forceinline__ void compute_tile(WaveState<D>& w, const char* sk, co
   w.l_run += ls[0] + ls[1];
 
   // ---- O^T += V^T P^T over the active 32-key blocks (a uniform choice per tile) ----
-  if (act[1]) pv_blocks<D, 2>(w, sv, pb);
-  else if (act[0]) pv_blocks<D, 1>(w, sv, pb);
+  if (lead) __builtin_amdgcn_s_setprio(2);
+  pv_blocks<D, 2>(w, sv, pb);
+  if (lead) __builtin_amdgcn_s_setprio(0);
+}
+
+// Work item -> (batch, query head, pair). Workgroups are dispatched to the 8 XCDs round
+// robin; this gives XCD x a contiguous run of items, so the items of one KV head (adjacent
+// query heads of one batch) share that XCD's L2.
+__device__ __forceinline__ int xcd_item(int id, int n) {
+  constexpr int kXcd = 8;
+  const int x = id % kXcd, s = id / kXcd;
+  const int q = n / kXcd, r = n % kXcd;
+  return x < r ? x * (q + 1) + s : r * (q + 1) + (x - r) * q + s;
 }
 
 template <int D, bool CAUSAL>
-__device__ __forceinline__ void fwd_bf16_body(const FwdArgs& a) {
-  using G = Geo<D>;
+__device__ __forceinline__ void fwd_tile_body(const FwdArgs& a) {
+  using G = Geo<D, 4>;
   // two stages, each a K tile and a V tile; separate objects so the compiler can tell the
   // in-flight direct loads into one stage from the reads of the other
   __shared__ __attribute__((aligned(1024))) char sk0[G::kTile];
@@ -369,7 +399,7 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs& a) {
   const int my_q = qw + l32;
   const int wave_last_key = qw + 31 + off;   // last key any query of this wave may see
 
-  TileDma<D> dma;
+  TileDma<D, 4> dma;
   dma.init(wave, lane, kbase, vbase, a.Sk);
   if (ntiles > 0) dma.issue(sk0, sv0, 0, a.Sk);
   wait_dma_and_barrier();
@@ -377,13 +407,14 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs& a) {
   for (int j = 0; j < ntiles; j += 2) {
     // stage 0 holds tile j; prefetch tile j+1 into stage 1
     if (j + 1 < ntiles) dma.issue(sk1, sv1, (j + 1) * kBN, a.Sk);
-    compute_tile<D, CAUSAL>(w, sk0, sv0, j * kBN, a.Sk, qw, wave_last_key, my_q, off, h, c);
+    compute_tile<D, CAUSAL>(w, sk0, sv0, j * kBN, a.Sk, qw, wave_last_key, my_q, off, h, c,
+                            false);
     wait_dma_and_barrier();
     if (j + 1 >= ntiles) break;
     // stage 1 holds tile j+1; prefetch tile j+2 into stage 0
     if (j + 2 < ntiles) dma.issue(sk0, sv0, (j + 2) * kBN, a.Sk);
     compute_tile<D, CAUSAL>(w, sk1, sv1, (j + 1) * kBN, a.Sk, qw, wave_last_key, my_q, off, h,
-                            c);
+                            c, false);
     wait_dma_and_barrier();
   }
 
@@ -408,16 +439,231 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs& a) {
   }
 }
 
-// The four instances are plain kernels (not a kernel template): their host-side launch stubs
-// then depend only on these signatures.
-#define ATTN_FWD_KERNEL(NAME, D, CAUSAL)                                                  \
-  __global__ __launch_bounds__(kThreads)                                                  \
-  __attribute__((amdgpu_waves_per_eu(ATTN_FWD_WAVES_PER_EU, ATTN_FWD_WAVES_PER_EU)))    \
-  void NAME(FwdArgs a) { fwd_bf16_body<D, CAUSAL>(a); }
-ATTN_FWD_KERNEL(fwd_bf16_d128_causal, 128, true)
-ATTN_FWD_KERNEL(fwd_bf16_d128, 128, false)
-ATTN_FWD_KERNEL(fwd_bf16_d64_causal, 64, true)
-ATTN_FWD_KERNEL(fwd_bf16_d64, 64, false)
+template <int D, bool CAUSAL>
+__device__ __forceinline__ void fwd_pair_body(const FwdArgs& a) {
+  using G = Geo<D, 8>;
+  // two K/V streams x two stages; separate objects so the compiler can tell the in-flight
+  // direct loads into one stage from the reads of another
+  __shared__ __attribute__((aligned(1024))) char ska0[G::kTile];
+  __shared__ __attribute__((aligned(1024))) char sva0[G::kTile];
+  __shared__ __attribute__((aligned(1024))) char ska1[G::kTile];
+  __shared__ __attribute__((aligned(1024))) char sva1[G::kTile];
+  __shared__ __attribute__((aligned(1024))) char skb0[G::kTile];
+  __shared__ __attribute__((aligned(1024))) char svb0[G::kTile];
+  __shared__ __attribute__((aligned(1024))) char skb1[G::kTile];
+  __shared__ __attribute__((aligned(1024))) char svb1[G::kTile];
+  __shared__ float xml[4][2][64];     // hand-over of (mref, l_run) from the L waves
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = wave_uniform(tid >> 6);
+  const int l32 = lane & 31;
+  const int h = lane >> 5;
+  const bool lwave = wave < 4;           // L wave (light rows, then the heavy tail)
+  const int wr = wave & 3;               // 32-row block of a tile
+
+  // ---- work item ----
+  const int item = xcd_item(blockIdx.x, a.nitems);
+  const int pair = item % a.npairs;
+  const int bh = item / a.npairs;
+  const int b = bh / a.Hq;
+  const int hq = bh - b * a.Hq;
+  const int hk = hq / a.group;
+  int tl, th;
+  bool single;
+  if (CAUSAL) {
+    tl = pair;
+    th = a.ntq - 1 - pair;
+    single = tl == th;
+  } else {
+    tl = 2 * pair;
+    th = 2 * pair + 1;
+    single = th >= a.ntq;
+  }
+  if (single) th = tl;                   // the only tile is the heavy one; no light rows
+  const int off = a.Sk - a.Sq;           // causal diagonal offset
+
+  // K/V tiles holding a key that some row of tile t sees
+  auto tiles_for = [&](int t) -> int {
+    const int last = min(t * kBM + kBM, a.Sq) - 1;
+    int kend = a.Sk;
+    if (CAUSAL) kend = min(a.Sk, max(0, last + off + 1));
+    return (kend + kBN - 1) / kBN;
+  };
+  const int nH = tiles_for(th);
+  const int nL = single ? 0 : tiles_for(tl);
+  const int x = (nL + nH + 1) / 2;       // steps; the H waves take key tiles [0, x)
+  const int nB = nH - x;                 // key tiles [x, nH) of the heavy rows go to the L waves
+
+  const uint16_t* qbase = a.q + ((size_t)(b * a.Hq + hq) * a.Sq) * D;
+  const uint16_t* kbase = a.k + ((size_t)(b * a.Hkv + hk) * a.Sk) * D;
+  const uint16_t* vbase = a.v + ((size_t)(b * a.Hkv + hk) * a.Sk) * D;
+
+  WaveState<D> w;
+  // K operand: row l32 (+32kb), chunk 2kk+h at its permuted slot
+#pragma unroll
+  for (int kk = 0; kk < G::KS; ++kk)
+    w.koff[kk] = l32 * G::kRow + (((2 * kk + h) ^ kswz<D>(l32)) * 16);
+  // V^T operand via transposed reads: source lane (group g, index j) points at key
+  // 4*(g/2) + j/4 (+ the block's first key) and columns 32db + 16*(g%2) + 4*(j%4) .. +3
+  {
+    const int g = lane >> 4, j = lane & 15;
+    const int keyl = 4 * (g >> 1) + (j >> 2);
+    const int small = 2 * (g & 1) + ((j & 3) >> 1);
+#pragma unroll
+    for (int db = 0; db < G::DB; ++db)
+      w.voff[db] = keyl * G::kRow + (((4 * db + small) ^ vswz<D>(keyl)) * 16) + 8 * (j & 1);
+  }
+  const float c = a.c;
+
+  // rows of the wave: qw .. qw + 31
+  auto begin_rows = [&](int qw) {
+    const int qi = qw + l32;
+#pragma unroll
+    for (int kk = 0; kk < G::KS; ++kk) {
+      if (qi < a.Sq)
+        w.qf[kk] = *reinterpret_cast<const u32x4*>(qbase + (size_t)qi * D + kk * 16 + h * 8);
+      else
+        w.qf[kk] = u32x4{0, 0, 0, 0};
+    }
+    // Consume the Q loads here: otherwise the loop's first use of qf must wait for every
+    // outstanding global load, including the next tile's prefetch.
+#pragma unroll
+    for (int kk = 0; kk < G::KS; ++kk) asm volatile("" : "+v"(w.qf[kk]));
+#pragma unroll
+    for (int i = 0; i < G::DB; ++i) w.o[i] = f32x16{};
+    w.mref = -INFINITY;
+    w.l_run = 0.f;
+  };
+  // normalise and store O (bf16) and LSE (natural log) of the rows qw .. qw + 31
+  auto store_rows = [&](int qw) {
+    const int my_q = qw + l32;
+    const float l_tot = xor32_sum(w.l_run);
+    const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
+    if (my_q < a.Sq) {
+      uint16_t* orow = a.o + ((size_t)(b * a.Hq + hq) * a.Sq + my_q) * D;
+#pragma unroll
+      for (int db = 0; db < G::DB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d = 32 * db + 8 * g + 4 * h;
+          u32x2 v = {pack_bf16x2(w.o[db][4 * g + 0] * inv, w.o[db][4 * g + 1] * inv),
+                     pack_bf16x2(w.o[db][4 * g + 2] * inv, w.o[db][4 * g + 3] * inv)};
+          *reinterpret_cast<u32x2*>(orow + d) = v;
+        }
+      if (a.lse != nullptr && h == 0) {
+        const float lse = (l_tot > 0.f) ? (w.mref + log2_fast(l_tot)) * kLn2 : -INFINITY;
+        a.lse[(size_t)(b * a.Hq + hq) * a.Sq + my_q] = lse;
+      }
+    }
+  };
+
+  const int qlight = tl * kBM + 32 * wr;
+  const int qheavy = th * kBM + 32 * wr;
+  int qw;                                 // rows the wave is working on
+  if (lwave && !single) {
+    qw = qlight;
+    begin_rows(qw);
+    if (nL == 0) {                        // light rows that see no key at all
+      store_rows(qw);
+      qw = qheavy;
+      begin_rows(qw);
+    }
+  } else {
+    qw = qheavy;
+    begin_rows(qw);
+  }
+
+  TileDma<D, 8> dma;
+  dma.init(wave, lane, kbase, vbase, a.Sk);
+  // step j: stream A holds key tile j (H waves, and L waves while j < nL); stream B holds key
+  // tile nH + nL - 1 - j (L waves, once past their light rows: the heavy tail walked from its
+  // end, which with the causal pairing is tile 2T + 1 - j for every pair, so the workgroups
+  // running side by side read the same two tiles at each step and share them in L2)
+  auto prefetch = [&](int j, char* ska, char* sva, char* skb, char* svb) {
+    if (j >= x) return;
+    dma.issue(ska, sva, j * kBN, a.Sk);
+    if (j >= nL && j - nL < nB) dma.issue(skb, svb, (nH + nL - 1 - j) * kBN, a.Sk);
+  };
+  auto step = [&](int j, const char* ska, const char* sva, const char* skb, const char* svb) {
+    const char *sk, *sv;
+    int kt;
+    if (!lwave) {
+      sk = ska; sv = sva; kt = j * kBN;
+    } else if (j < nL) {
+      sk = ska; sv = sva; kt = j * kBN;
+    } else if (j - nL < nB) {
+      sk = skb; sv = svb; kt = (nH + nL - 1 - j) * kBN;
+    } else {
+      return;                             // this L wave has no tile at this step
+    }
+    const int wave_last_key = qw + 31 + off;   // last key any query of this wave may see
+    if (!CAUSAL || kt <= wave_last_key)
+      compute_tile<D, CAUSAL>(w, sk, sv, kt, a.Sk, qw, wave_last_key, qw + l32, off, h, c, lwave);
+    if (lwave && j == nL - 1) {           // light rows done: store them, move to the heavy tail
+      store_rows(qw);
+      if (nB > 0) {
+        qw = qheavy;
+        begin_rows(qw);
+      }
+    }
+  };
+
+  prefetch(0, ska0, sva0, skb0, svb0);
+  wait_dma_and_barrier();
+  for (int j = 0; j < x; j += 2) {
+    // stage 0 holds step j; prefetch step j+1 into stage 1
+    prefetch(j + 1, ska1, sva1, skb1, svb1);
+    step(j, ska0, sva0, skb0, svb0);
+    wait_dma_and_barrier();
+    if (j + 1 >= x) break;
+    prefetch(j + 2, ska0, sva0, skb0, svb0);
+    step(j + 1, ska1, sva1, skb1, svb1);
+    wait_dma_and_barrier();
+  }
+
+  // ---- merge the heavy rows' two partial states, store ----
+  if (nB > 0) {
+    // (every stage is free after the loop's final barrier)
+    float* xo = reinterpret_cast<float*>(wr == 0 ? ska0 : wr == 1 ? sva0 : wr == 2 ? ska1 : sva1);
+    if (lwave) {
+#pragma unroll
+      for (int db = 0; db < G::DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xo[(16 * db + r) * 64 + lane] = w.o[db][r];
+      xml[wr][0][lane] = w.mref;
+      xml[wr][1][lane] = w.l_run;
+    }
+    __syncthreads();
+    if (!lwave) {
+      const float m2 = xml[wr][0][lane], l2 = xml[wr][1][lane];
+      const float mn = fmaxf(w.mref, m2);
+      const float a1 = (w.mref == -INFINITY) ? 0.f : exp2_fast(w.mref - mn);
+      const float a2 = (m2 == -INFINITY) ? 0.f : exp2_fast(m2 - mn);
+      w.mref = mn;
+      w.l_run = w.l_run * a1 + l2 * a2;
+#pragma unroll
+      for (int db = 0; db < G::DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          w.o[db][r] = w.o[db][r] * a1 + xo[(16 * db + r) * 64 + lane] * a2;
+    }
+  }
+  if (!lwave) store_rows(qw);
+}
+
+// Plain kernels (not kernel templates): their host-side launch stubs then depend only on these
+// signatures.
+#define ATTN_FWD_KERNEL(NAME, BODY, WAVES, D, CAUSAL)                      \
+  __global__ __launch_bounds__(64 * WAVES)                                 \
+  __attribute__((amdgpu_waves_per_eu(2, 2)))                               \
+  void NAME(FwdArgs a) { BODY<D, CAUSAL>(a); }
+ATTN_FWD_KERNEL(fwd_bf16_d128_causal, fwd_tile_body, 4, 128, true)
+ATTN_FWD_KERNEL(fwd_bf16_d128, fwd_tile_body, 4, 128, false)
+ATTN_FWD_KERNEL(fwd_bf16_d64_causal, fwd_tile_body, 4, 64, true)
+ATTN_FWD_KERNEL(fwd_bf16_d64, fwd_tile_body, 4, 64, false)
+ATTN_FWD_KERNEL(fwd_bf16_d128_causal_pairs, fwd_pair_body, 8, 128, true)
+ATTN_FWD_KERNEL(fwd_bf16_d64_causal_pairs, fwd_pair_body, 8, 64, true)
 #undef ATTN_FWD_KERNEL
 
 }  // namespace
@@ -432,22 +678,30 @@ hipError_t launch_fwd_bf16(const FwdProblem& p, hipStream_t stream) {
   a.B = p.B; a.Hq = p.Hq; a.Hkv = p.Hkv; a.Sq = p.Sq; a.Sk = p.Sk;
   a.group = p.Hq / p.Hkv;
   a.ntq = (p.Sq + kBM - 1) / kBM;
-  a.causal = p.causal;
+  a.npairs = (a.ntq + 1) / 2;
   float c = p.scale * kLog2e;
   // scale == 0 means uniform weights; any tiny positive c gives exactly that (every exp2
   // argument rounds to 0) while keeping -inf * c = -inf for masked keys.
   if (!(c > 0.f)) c = 1.17549435e-38f;
   a.c = c;
-  const long long nwg = (long long)a.ntq * p.B * p.Hq;
+  const bool pairs = p.causal && a.ntq <= kPairMaxTiles;
+  const long long nwg = (long long)(pairs ? a.npairs : a.ntq) * p.B * p.Hq;
   if (nwg == 0) return hipSuccess;
   if (nwg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  dim3 grid((unsigned)nwg), block(kThreads);
-  if (p.D == 128) {
-    if (p.causal) hipLaunchKernelGGL(fwd_bf16_d128_causal, grid, block, 0, stream, a);
-    else hipLaunchKernelGGL(fwd_bf16_d128, grid, block, 0, stream, a);
+  a.nitems = (int)nwg;
+  if (pairs) {
+    dim3 grid((unsigned)nwg), block(512);
+    if (p.D == 128) hipLaunchKernelGGL(fwd_bf16_d128_causal_pairs, grid, block, 0, stream, a);
+    else hipLaunchKernelGGL(fwd_bf16_d64_causal_pairs, grid, block, 0, stream, a);
   } else {
-    if (p.causal) hipLaunchKernelGGL(fwd_bf16_d64_causal, grid, block, 0, stream, a);
-    else hipLaunchKernelGGL(fwd_bf16_d64, grid, block, 0, stream, a);
+    dim3 grid((unsigned)nwg), block(256);
+    if (p.D == 128) {
+      if (p.causal) hipLaunchKernelGGL(fwd_bf16_d128_causal, grid, block, 0, stream, a);
+      else hipLaunchKernelGGL(fwd_bf16_d128, grid, block, 0, stream, a);
+    } else {
+      if (p.causal) hipLaunchKernelGGL(fwd_bf16_d64_causal, grid, block, 0, stream, a);
+      else hipLaunchKernelGGL(fwd_bf16_d64, grid, block, 0, stream, a);
+    }
   }
   return hipGetLastError();
 }

@@ -12,7 +12,8 @@ Inputs are generated once, uploaded, and resident in HBM before timing starts.
 Printed (one JSON line): ``value`` is the prefill kernel's throughput in TFLOP/s counting
 4*D flops per visible (query, key) pair (causal-adjusted); ``decode`` gives the decode KV
 bandwidth in GB/s counting each visible token's K and V once plus q, o and the block table.
-Kernel durations come from HIP events recorded around each launch on the launch stream.
+Kernel durations come from HIP events recorded around each launch on the launch stream
+(created without the system-scope fence, so recording them adds no cache flush between kernels).
 ``roofline`` compares the prefill kernel with the bf16 dense MFMA peak, ``decode.roofline``
 the decode with the HBM peak. ``cpu_baseline`` times the fp64 CPU oracle on the host on the
 same prefill workload.
@@ -85,6 +86,54 @@ def measured_traffic(kernel_tag: str, digest: str):
     return float(m_t.group(1))
 
 
+class HipEvents:
+    """Timing events from the HIP runtime torch already loaded, created with
+    hipEventDisableSystemFence: recording one then costs no system-scope cache writeback and
+    invalidation, which with ordinary events adds a bubble of several microseconds in front
+    of the next kernel and slows it (the HIP header documents the flag for exactly this)."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self, n):
+        import ctypes
+        import torch  # noqa: F401  (maps the runtime)
+        import exact_attention_42_amd as A
+        rts = A._hip_runtimes_mapped()
+        if len(rts) != 1:
+            raise RuntimeError(f"expected one HIP runtime in the process, found {rts}")
+        self._ct = ctypes
+        self._hip = ctypes.CDLL(rts[0])
+        self._hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self._hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self._hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                  ctypes.c_void_p]
+        self._hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.ev = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            rc = self._hip.hipEventCreateWithFlags(ctypes.byref(e), self.DISABLE_SYSTEM_FENCE)
+            if rc != 0:
+                raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+            self.ev.append(e)
+
+    def record(self, i, stream):
+        rc = self._hip.hipEventRecord(self.ev[i], self._ct.c_void_p(stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def elapsed_ms(self, i, j):
+        t = self._ct.c_float()
+        rc = self._hip.hipEventElapsedTime(self._ct.byref(t), self.ev[i], self.ev[j])
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return float(t.value)
+
+    def close(self):
+        for e in self.ev:
+            self._hip.hipEventDestroy(e)
+        self.ev = []
+
+
 def cpu_baseline(min_seconds: float):
     """The fp64 oracle (as it stands) on the prefill workload, repeated until min_seconds."""
     import oracle
@@ -143,15 +192,18 @@ def main():
     del d
     scale_p, scale_d = float(PREFILL.scale), float(DECODE.scale)
 
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record()
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def step(i=None):
+        # events i0 | prefill | i1 | decode (split + combine) | i2, all on the launch stream
+        if i is not None:
+            ev.record(3 * i, stream)
         A.attn_fwd(qg, kg, vg, causal=True, scale=scale_p, out=o, lse=lse)
-        if ev is not None:
-            ev[1].record()
+        if i is not None:
+            ev.record(3 * i + 1, stream)
         A.attn_decode_paged(dq, dkc, dvc, dbt, dctx, scale=scale_d, out=do)
-        if ev is not None:
-            ev[2].record()
+        if i is not None:
+            ev.record(3 * i + 2, stream)
 
     if args.calibrate_copy_mib > 0:
         n = args.calibrate_copy_mib << 20
@@ -164,16 +216,17 @@ def main():
 
     for _ in range(args.warmup):
         step()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    ev = HipEvents(3 * args.steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(events[i])
+        step(i)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
 
-    fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
-    dec_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
+    fwd_ms = float(np.mean([ev.elapsed_ms(3 * i, 3 * i + 1) for i in range(args.steps)]))
+    dec_ms = float(np.mean([ev.elapsed_ms(3 * i + 1, 3 * i + 2) for i in range(args.steps)]))
+    ev.close()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     flops = prefill_flops(PREFILL)
     tflops = flops / (fwd_ms * 1e-3) / 1e12
@@ -181,7 +234,7 @@ def main():
     gbs = dbytes / (dec_ms * 1e-3) / 1e9
 
     fwd_digest = source_digest("attn_fwd_bf16.hip", "cdna4.hpp")
-    dec_digest = source_digest("attn_decode.hip", "cdna4.hpp")
+    dec_digest = source_digest("attn_decode.hip", "cdna4.hpp", "attn_api.hip")
     out = {
         "metric": "fwd attention TFLOP/s & % MFMA peak (prefill); decode KV GB/s & % HBM peak",
         "value": round(tflops, 2),

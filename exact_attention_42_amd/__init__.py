@@ -33,7 +33,7 @@ _SIGNATURES = {
     "attn_decode_paged_ex": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I,
                                   _I, _P, _Z, _P]),
     "attn_decode_workspace_bytes": (_Z, [_I, _I, _I, _I]),
-    "attn_decode_default_splits": (_I, []),
+    "attn_decode_default_splits": (_I, [_I, _I]),
     "attn_status_string": (ctypes.c_char_p, [_I]),
     "attn_last_error": (ctypes.c_char_p, []),
     "attn_release_workspace": (None, []),
@@ -105,8 +105,8 @@ def attn_abi_version() -> int:
     return load_library().attn_abi_version()
 
 
-def attn_decode_default_splits() -> int:
-    return load_library().attn_decode_default_splits()
+def attn_decode_default_splits(B: int, Hq: int) -> int:
+    return load_library().attn_decode_default_splits(B, Hq)
 
 
 def attn_decode_workspace_bytes(B: int, Hq: int, D: int, max_splits: int = 0) -> int:

@@ -96,13 +96,20 @@ struct Workspace {
 std::mutex g_ws_mutex;
 std::map<std::pair<int, void*>, Workspace> g_ws;
 
-int default_splits() {
-  static int v = [] {
+// Split-KV bound when the caller passes 0: enough (query head, split) rows for a few rounds
+// of split workgroups on the whole GPU (~8192 rows), since fewer splits mean less partial-
+// result traffic and a cheaper combine. ATTN_DECODE_SPLITS (1..64) overrides it.
+int default_splits(int B, int Hq) {
+  static const int env = [] {
     const char* s = std::getenv("ATTN_DECODE_SPLITS");
-    int x = s ? std::atoi(s) : 0;
-    return (x >= 1 && x <= 64) ? x : 16;
+    const int x = s ? std::atoi(s) : 0;
+    return (x >= 1 && x <= 64) ? x : 0;
   }();
-  return v;
+  if (env) return env;
+  const long long rows = (long long)B * Hq;
+  if (rows <= 0) return 1;
+  const long long s = (8192 + rows - 1) / rows;
+  return (int)(s < 1 ? 1 : (s > 64 ? 64 : s));
 }
 
 size_t ws_bytes(int B, int Hq, int D, int splits) {
@@ -156,7 +163,7 @@ int run_decode(const void* q, const void* k_cache, const void* v_cache,
   if (int rc = check_scale(scale)) return rc;
   if (max_splits < 0 || max_splits > 64)
     return fail(ATTN_ERR_SHAPE, "max_splits must be in 0..64 (got %d)", max_splits);
-  const int splits = max_splits ? max_splits : default_splits();
+  const int splits = max_splits ? max_splits : default_splits(B, Hq);
   if (B == 0) return ok();
   if (!q || !k_cache || !v_cache || !block_table || !ctx_lens || !o)
     return fail(ATTN_ERR_NULL, "q, k_cache, v_cache, block_table, ctx_lens and o must not be NULL");
@@ -220,10 +227,10 @@ int attn_decode_paged_ex(const void* q, const void* k_cache, const void* v_cache
 
 size_t attn_decode_workspace_bytes(int B, int Hq, int D, int max_splits) {
   if (B < 0 || Hq < 0 || D < 0 || max_splits < 0 || max_splits > 64) return 0;
-  return ws_bytes(B, Hq, D, max_splits ? max_splits : default_splits());
+  return ws_bytes(B, Hq, D, max_splits ? max_splits : default_splits(B, Hq));
 }
 
-int attn_decode_default_splits(void) { return default_splits(); }
+int attn_decode_default_splits(int B, int Hq) { return default_splits(B, Hq); }
 
 const char* attn_status_string(int status) {
   switch (status) {
@@ -255,6 +262,6 @@ void attn_release_workspace(void) {
   if (have_cur) (void)hipSetDevice(cur);
 }
 
-int attn_abi_version(void) { return 1; }
+int attn_abi_version(void) { return 2; }
 
 }  // extern "C"

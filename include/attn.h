@@ -106,8 +106,10 @@ int attn_decode_paged_ex(const void* q, const void* k_cache, const void* v_cache
 /* Bytes of split workspace the decode needs (max_splits 0 = the default). */
 size_t attn_decode_workspace_bytes(int B, int Hq, int D, int max_splits);
 
-/* Default split-KV bound used when max_splits is 0. */
-int attn_decode_default_splits(void);
+/* Default split-KV bound used when max_splits is 0, for a batch of B sequences with Hq query
+ * heads: about 8192 / (B * Hq), clamped to 1..64 (the environment variable
+ * ATTN_DECODE_SPLITS = 1..64 overrides it). */
+int attn_decode_default_splits(int B, int Hq);
 
 /* Static text for a status code. */
 const char* attn_status_string(int status);
@@ -118,7 +120,7 @@ const char* attn_last_error(void);
 /* Frees the library-owned decode workspaces (synchronises the devices that hold them). */
 void attn_release_workspace(void);
 
-/* ABI version of this header: 1. */
+/* ABI version of this header: 2. */
 int attn_abi_version(void);
 
 #ifdef __cplusplus

@@ -42,7 +42,7 @@ def test_status_strings_and_version():
     for code in range(9):
         assert A.attn_status_string(code) not in ("", "unknown status")
     assert A.attn_status_string(99) == "unknown status"
-    assert A.attn_abi_version() == 1
+    assert A.attn_abi_version() == 2
 
 
 def fwd(*, q=P, k=P, v=P, o=P, lse=0, B=1, Hq=32, Hkv=8, Sq=128, Sk=128, D=128, causal=1,
@@ -110,8 +110,18 @@ def test_decode_plain_entry_point_rejects_before_launch():
     assert dec(ex=False, B=0) == OK
 
 
+def test_decode_default_splits():
+    # about 8192 (query head, split) rows per launch, clamped to 1..64
+    assert A.attn_decode_default_splits(64, 32) == 4
+    assert A.attn_decode_default_splits(8, 32) == 32
+    assert A.attn_decode_default_splits(1, 32) == 64
+    assert A.attn_decode_default_splits(1, 1) == 64
+    assert A.attn_decode_default_splits(512, 64) == 1
+    assert A.attn_decode_default_splits(0, 32) == 1
+
+
 def test_decode_workspace_size():
-    d = A.attn_decode_default_splits()
+    d = A.attn_decode_default_splits(64, 32)
     assert 1 <= d <= 64
     assert A.attn_decode_workspace_bytes(64, 32, 128, 0) == 64 * 32 * d * 129 * 4
     assert A.attn_decode_workspace_bytes(3, 5, 64, 7) == 3 * 5 * 7 * 65 * 4

@@ -48,6 +48,11 @@ SMALL = [
     (1, 2, 2, 70, 1, 128, False),         # one key
     (3, 2, 1, 129, 63, 64, False),        # Sk below one tile
     (1, 4, 4, 512, 512, 128, True),       # several full tiles, MHA
+    # causal launches with few tiles per head take the paired-tile kernel
+    (1, 2, 1, 1100, 1100, 128, True),     # 9 tiles: four pairs and one tile on its own
+    (1, 2, 1, 900, 400, 128, True),       # Sq > Sk: whole light tiles see no key
+    (1, 8, 2, 1000, 1000, 64, True),      # D = 64, GQA 4:1
+    (2, 2, 2, 640, 700, 128, True),       # Sq < Sk, ragged heavy tail
 ]
 
 
@@ -135,6 +140,21 @@ def test_config_batched_b8_s4096_sampled(dev):
 def test_config_long_s32768_sampled(dev):
     """B=1, Hq=32, Hkv=8, S=32768, D=128, bf16 x0.5, causal at full size."""
     _full_size_check("long_s32768", dev, nrows=256)
+
+
+@pytest.mark.parametrize("ntiles", [64, 65])
+def test_causal_kernel_switch_sampled(ntiles, dev):
+    """Causal launches with up to 64 query tiles of 128 rows per head run the paired-tile kernel,
+    longer ones the one-tile-per-workgroup kernel; both sides of the switch, on sampled rows."""
+    S = 128 * ntiles
+    q, k, v = W.fwd_inputs(1, 2, 1, S, S, 128, seed=1000 + ntiles)
+    o, lse = run_bf16(q, k, v, True, np.float32(1 / np.sqrt(128)), dev)
+    edges = [0, 1, 127, 128, S // 2 - 1, S // 2, S // 2 + 127, S - 129, S - 128, S - 1]
+    rows = W.sample_rows(1, 2, S, 96, seed=ntiles, must=edges)
+    O, L = oracle.attention_rows(q, k, v, rows, causal=True, scale=np.float32(1 / np.sqrt(128)))
+    idx = tuple(np.array(rows).T)
+    check_bf16(o[idx], O, what=f"{ntiles} tiles sampled O")
+    check_lse(lse[idx], L, what=f"{ntiles} tiles sampled LSE")
 
 
 def test_scale_zero_and_no_keys(dev):

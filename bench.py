@@ -6,7 +6,7 @@ One step is one pass of the whole hot path over one batch of synthetic input:
     bf16, causal), then
   * decode:  attn_decode_paged on the paged workload (B=64, Hq=32, Hkv=8, D=128, contexts
     uniform in [512, 4096], 16-token blocks placed by a seeded permutation), which runs the
-    split-KV kernel and the LSE-merge combine kernel.
+    split-KV stream kernel and the LSE-merge combine kernel.
 Inputs are generated once, uploaded, and resident in HBM before timing starts.
 
 Printed (one JSON line): ``value`` is the prefill kernel's throughput in TFLOP/s counting
@@ -262,7 +262,7 @@ def main():
                    "roofline": {"bound": "hbm", "achieved": round(gbs, 1),
                                 "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                 "frac": round(gbs / PEAK_HBM_GBS, 4),
-                                "traffic": measured_traffic("decode_split_paged_decode_b64",
+                                "traffic": measured_traffic("decode_stream_paged_decode_b64",
                                                             dec_digest)}},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),

@@ -17,7 +17,7 @@ import os
 __all__ = [
     "AttnError", "library_path", "load_library",
     "attn_fwd", "attn_fwd_f32", "attn_decode_paged", "attn_decode_paged_ex",
-    "attn_decode_workspace_bytes", "attn_decode_default_splits", "attn_status_string",
+    "attn_decode_workspace_bytes", "attn_decode_default_workers", "attn_status_string",
     "attn_last_error", "attn_release_workspace", "attn_abi_version", "EXPORTED_SYMBOLS",
 ]
 
@@ -32,8 +32,8 @@ _SIGNATURES = {
     "attn_decode_paged": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P]),
     "attn_decode_paged_ex": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I,
                                   _I, _P, _Z, _P]),
-    "attn_decode_workspace_bytes": (_Z, [_I, _I, _I, _I]),
-    "attn_decode_default_splits": (_I, [_I, _I]),
+    "attn_decode_workspace_bytes": (_Z, [_I, _I, _I, _I, _I]),
+    "attn_decode_default_workers": (_I, []),
     "attn_status_string": (ctypes.c_char_p, [_I]),
     "attn_last_error": (ctypes.c_char_p, []),
     "attn_release_workspace": (None, []),
@@ -105,12 +105,12 @@ def attn_abi_version() -> int:
     return load_library().attn_abi_version()
 
 
-def attn_decode_default_splits(B: int, Hq: int) -> int:
-    return load_library().attn_decode_default_splits(B, Hq)
+def attn_decode_default_workers() -> int:
+    return load_library().attn_decode_default_workers()
 
 
-def attn_decode_workspace_bytes(B: int, Hq: int, D: int, max_splits: int = 0) -> int:
-    return load_library().attn_decode_workspace_bytes(B, Hq, D, max_splits)
+def attn_decode_workspace_bytes(B: int, Hq: int, Hkv: int, D: int, num_workers: int = 0) -> int:
+    return load_library().attn_decode_workspace_bytes(B, Hq, Hkv, D, num_workers)
 
 
 def attn_release_workspace() -> None:
@@ -231,12 +231,13 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, ctx_lens, scale=None, ou
 
 
 def attn_decode_paged_ex(q, k_cache, v_cache, block_table, ctx_lens, scale=None, out=None,
-                         lse=None, want_lse=True, check_blocks=True, max_splits=0,
+                         lse=None, want_lse=True, check_blocks=True, num_workers=0,
                          workspace=None, stream=None):
     """Paged decode with the explicit controls of the C ABI: returns (out, lse). The row
     stride of ``block_table`` is passed explicitly; ``check_blocks`` passes the pool size so
     out-of-range entries are skipped instead of read; ``workspace`` is an optional uint8
-    device tensor of at least attn_decode_workspace_bytes(B, Hq, D, max_splits) bytes."""
+    device tensor of at least attn_decode_workspace_bytes(B, Hq, Hkv, D, num_workers) bytes;
+    ``num_workers`` sets how many worker waves split the blocks (0 = the device default)."""
     torch = _torch()
     B, Hq, D, nb, Hkv, bs, dev = _decode_checks(q, k_cache, v_cache, block_table, ctx_lens)
     if out is None:
@@ -254,6 +255,6 @@ def attn_decode_paged_ex(q, k_cache, v_cache, block_table, ctx_lens, scale=None,
         _check(load_library().attn_decode_paged_ex(
             _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(ctx_lens), _ptr(out),
             _ptr(lse), B, Hq, Hkv, D, bs, float(scale), int(block_table.shape[1]),
-            int(nb) if check_blocks else 0, int(max_splits), _ptr(workspace),
+            int(nb) if check_blocks else 0, int(num_workers), _ptr(workspace),
             int(workspace.numel()) if workspace is not None else 0, _stream_ptr(dev, stream)))
     return out, lse

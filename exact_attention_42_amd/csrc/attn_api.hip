@@ -18,6 +18,8 @@ namespace {
 
 thread_local std::string g_last_error;
 
+constexpr int kMaxWorkers = 65536;
+
 int fail(int code, const char* fmt, ...) {
   char buf[512];
   va_list ap;
@@ -96,25 +98,25 @@ struct Workspace {
 std::mutex g_ws_mutex;
 std::map<std::pair<int, void*>, Workspace> g_ws;
 
-// Split-KV bound when the caller passes 0: enough (query head, split) rows for a few rounds
-// of split workgroups on the whole GPU (~8192 rows), since fewer splits mean less partial-
-// result traffic and a cheaper combine. ATTN_DECODE_SPLITS (1..64) overrides it.
-int default_splits(int B, int Hq) {
+// Worker waves when the caller passes 0: three per CU of the current device, which measured
+// fastest (more concurrent block streams only add memory-side contention; fewer leave HBM
+// idle). ATTN_DECODE_WORKERS (1..65536) overrides it.
+int default_workers() {
   static const int env = [] {
-    const char* s = std::getenv("ATTN_DECODE_SPLITS");
+    const char* s = std::getenv("ATTN_DECODE_WORKERS");
     const int x = s ? std::atoi(s) : 0;
-    return (x >= 1 && x <= 64) ? x : 0;
+    return (x >= 1 && x <= kMaxWorkers) ? x : 0;
   }();
   if (env) return env;
-  const long long rows = (long long)B * Hq;
-  if (rows <= 0) return 1;
-  const long long s = (8192 + rows - 1) / rows;
-  return (int)(s < 1 ? 1 : (s > 64 ? 64 : s));
-}
-
-size_t ws_bytes(int B, int Hq, int D, int splits) {
-  // partial outputs first (16-byte aligned start), then the partial log-sum-exps
-  return attn::decode_workspace_floats(B, Hq, D, splits) * sizeof(float);
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0) {
+    (void)hipGetLastError();
+    cus = 256;
+  }
+  const int w = 3 * cus;
+  return w > kMaxWorkers ? kMaxWorkers : w;
 }
 
 int get_workspace(void* stream, size_t need, void** out) {
@@ -146,7 +148,7 @@ int get_workspace(void* stream, size_t need, void** out) {
 int run_decode(const void* q, const void* k_cache, const void* v_cache,
                const int32_t* block_table, const int32_t* ctx_lens, void* o, float* lse, int B,
                int Hq, int Hkv, int D, int block_size, float scale, int table_stride,
-               int num_blocks, int max_splits, void* workspace, size_t workspace_bytes,
+               int num_blocks, int num_workers, void* workspace, size_t workspace_bytes,
                void* stream) {
   if (B < 0) return fail(ATTN_ERR_SHAPE, "B must be >= 0 (B=%d)", B);
   if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0)
@@ -161,9 +163,8 @@ int run_decode(const void* q, const void* k_cache, const void* v_cache,
   if (block_size != 16)
     return fail(ATTN_ERR_UNSUPPORTED, "block_size=%d not supported (16)", block_size);
   if (int rc = check_scale(scale)) return rc;
-  if (max_splits < 0 || max_splits > 64)
-    return fail(ATTN_ERR_SHAPE, "max_splits must be in 0..64 (got %d)", max_splits);
-  const int splits = max_splits ? max_splits : default_splits(B, Hq);
+  if (num_workers < 0 || num_workers > kMaxWorkers)
+    return fail(ATTN_ERR_SHAPE, "num_workers must be in 0..%d (got %d)", kMaxWorkers, num_workers);
   if (B == 0) return ok();
   if (!q || !k_cache || !v_cache || !block_table || !ctx_lens || !o)
     return fail(ATTN_ERR_NULL, "q, k_cache, v_cache, block_table, ctx_lens and o must not be NULL");
@@ -171,7 +172,8 @@ int run_decode(const void* q, const void* k_cache, const void* v_cache,
     return fail(ATTN_ERR_ALIGN, "q, k_cache, v_cache and o must be 16-byte aligned");
   if (!aligned(block_table, 4) || !aligned(ctx_lens, 4) || (lse && !aligned(lse, 4)))
     return fail(ATTN_ERR_ALIGN, "block_table, ctx_lens and lse must be 4-byte aligned");
-  const size_t need = ws_bytes(B, Hq, D, splits);
+  const int workers = num_workers ? num_workers : default_workers();
+  const size_t need = attn::decode_workspace_bytes(B, Hkv, Hq / Hkv, D, workers);
   void* ws = workspace;
   if (ws) {
     if (workspace_bytes < need)
@@ -185,10 +187,9 @@ int run_decode(const void* q, const void* k_cache, const void* v_cache,
   p.q = q; p.k_cache = k_cache; p.v_cache = v_cache;
   p.block_table = block_table; p.ctx_lens = ctx_lens; p.o = o; p.lse = lse;
   p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.D = D; p.block_size = block_size;
-  p.table_stride = table_stride; p.num_blocks = num_blocks; p.max_splits = splits;
+  p.table_stride = table_stride; p.num_blocks = num_blocks; p.workers = workers;
   p.scale = scale;
-  p.ws_o = static_cast<float*>(ws);
-  p.ws_lse = p.ws_o + (size_t)B * Hq * splits * D;
+  p.workspace = ws;
   hipError_t e = attn::launch_decode_paged(p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "attn_decode_paged launch");
   return ok();
@@ -218,19 +219,22 @@ int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
 int attn_decode_paged_ex(const void* q, const void* k_cache, const void* v_cache,
                          const int32_t* block_table, const int32_t* ctx_lens, void* o,
                          float* lse, int B, int Hq, int Hkv, int D, int block_size,
-                         float scale, int table_stride, int num_blocks, int max_splits,
+                         float scale, int table_stride, int num_blocks, int num_workers,
                          void* workspace, size_t workspace_bytes, void* stream) {
   return run_decode(q, k_cache, v_cache, block_table, ctx_lens, o, lse, B, Hq, Hkv, D,
-                    block_size, scale, table_stride, num_blocks, max_splits, workspace,
+                    block_size, scale, table_stride, num_blocks, num_workers, workspace,
                     workspace_bytes, stream);
 }
 
-size_t attn_decode_workspace_bytes(int B, int Hq, int D, int max_splits) {
-  if (B < 0 || Hq < 0 || D < 0 || max_splits < 0 || max_splits > 64) return 0;
-  return ws_bytes(B, Hq, D, max_splits ? max_splits : default_splits(B, Hq));
+size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int D, int num_workers) {
+  if (B < 0 || B > 65535 || Hq < 1 || Hkv < 1 || Hkv > 65535 || Hq % Hkv != 0 ||
+      Hq / Hkv > 16 || (D != 64 && D != 128) || num_workers < 0 || num_workers > kMaxWorkers)
+    return 0;
+  return attn::decode_workspace_bytes(B, Hkv, Hq / Hkv, D,
+                                      num_workers ? num_workers : default_workers());
 }
 
-int attn_decode_default_splits(int B, int Hq) { return default_splits(B, Hq); }
+int attn_decode_default_workers(void) { return default_workers(); }
 
 const char* attn_status_string(int status) {
   switch (status) {
@@ -262,6 +266,6 @@ void attn_release_workspace(void) {
   if (have_cur) (void)hipSetDevice(cur);
 }
 
-int attn_abi_version(void) { return 2; }
+int attn_abi_version(void) { return 3; }
 
 }  // extern "C"

@@ -35,13 +35,13 @@ struct DecodeProblem {
   int B, Hq, Hkv, D, block_size;
   int table_stride;         // <= 0: derived on the device as max_b ceil(ctx_b / block_size)
   int num_blocks;           // <= 0: unknown (no physical-block range check)
-  int max_splits;           // split-KV partitions per sequence (upper bound)
+  int workers;              // worker waves that split the batch's K/V blocks between them
   float scale;
-  float* ws_o;              // [B, Hq, max_splits, D] fp32 partial outputs
-  float* ws_lse;            // [B, Hq, max_splits] fp32 partial log-sum-exps
+  void* workspace;          // decode_workspace_bytes(B, Hkv, Hq / Hkv, D, workers) bytes
 };
 
-size_t decode_workspace_floats(int B, int Hq, int D, int max_splits);
+// Bytes of partial results the decode needs (16-byte aligned start assumed).
+size_t decode_workspace_bytes(int B, int Hkv, int group, int D, int workers);
 hipError_t launch_decode_paged(const DecodeProblem& p, hipStream_t stream);
 
 }  // namespace attn

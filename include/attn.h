@@ -79,9 +79,11 @@ int attn_fwd_f32(const void* q, const void* k, const void* v, void* o, float* ls
  *   ctx_lens:  [B] int32, number of cached tokens of each sequence (the new token included).
  *              Values <= 0 give O = 0. No mask is applied inside the context.
  * block_size must be 16. Hq / Hkv must be at most 16. The call runs two kernels on stream:
- * a split-KV kernel writing per-split partial results to a library-owned workspace (one per
- * device and stream, grown on demand; growing it synchronises the device) and a combine
- * kernel merging them by their log-sum-exps. The caller must keep physical block ids valid;
+ * a streaming kernel in which W worker waves split the batch's (sequence, KV head, block)
+ * list into equal contiguous shares and write partial results (running max, sum and
+ * unnormalised output) to a library-owned workspace (one per device and stream, grown on
+ * demand; growing it synchronises the device), and a combine kernel merging each sequence's
+ * partials with the running-softmax algebra. The caller must keep physical block ids valid;
  * they are not range-checked here (attn_decode_paged_ex can check them). */
 int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
                       const int32_t* block_table, const int32_t* ctx_lens, void* o,
@@ -93,23 +95,27 @@ int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
  *   table_stride:    row stride of block_table in entries; <= 0 derives it as above
  *   num_blocks:      size of the physical pool; > 0 makes the kernels skip (treat as empty)
  *                    any block-table entry outside [0, num_blocks); <= 0 = unchecked
- *   max_splits:      upper bound on split-KV partitions per sequence, 1..64; 0 = default
+ *   num_workers:     worker waves W that split the blocks, 1..65536; 0 = the default
+ *                    (attn_decode_default_workers()). Any W gives the same result up to
+ *                    rounding; it only changes how the work is spread.
  *   workspace:       caller-owned device buffer of at least
- *                    attn_decode_workspace_bytes(B, Hq, D, max_splits) bytes, 16-byte
- *                    aligned; NULL = use the library-owned workspace */
+ *                    attn_decode_workspace_bytes(B, Hq, Hkv, D, num_workers) bytes, 16-byte
+ *                    aligned; NULL = use the library-owned workspace. Calls sharing one
+ *                    workspace must not overlap in time. */
 int attn_decode_paged_ex(const void* q, const void* k_cache, const void* v_cache,
                          const int32_t* block_table, const int32_t* ctx_lens, void* o,
                          float* lse, int B, int Hq, int Hkv, int D, int block_size,
-                         float scale, int table_stride, int num_blocks, int max_splits,
+                         float scale, int table_stride, int num_blocks, int num_workers,
                          void* workspace, size_t workspace_bytes, void* stream);
 
-/* Bytes of split workspace the decode needs (max_splits 0 = the default). */
-size_t attn_decode_workspace_bytes(int B, int Hq, int D, int max_splits);
+/* Bytes of workspace the decode needs (num_workers 0 = the default):
+ * (W + B * Hkv) partial results of (Hq / Hkv) heads x (D + 2) floats, 16-byte padded, plus
+ * 2 int32 per (sequence, KV head). 0 for invalid arguments. */
+size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int D, int num_workers);
 
-/* Default split-KV bound used when max_splits is 0, for a batch of B sequences with Hq query
- * heads: about 8192 / (B * Hq), clamped to 1..64 (the environment variable
- * ATTN_DECODE_SPLITS = 1..64 overrides it). */
-int attn_decode_default_splits(int B, int Hq);
+/* Default worker-wave count for the current device: 3 per compute unit. The environment
+ * variable ATTN_DECODE_WORKERS = 1..65536 overrides it. */
+int attn_decode_default_workers(void);
 
 /* Static text for a status code. */
 const char* attn_status_string(int status);
@@ -120,7 +126,7 @@ const char* attn_last_error(void);
 /* Frees the library-owned decode workspaces (synchronises the devices that hold them). */
 void attn_release_workspace(void);
 
-/* ABI version of this header: 2. */
+/* ABI version of this header: 3. */
 int attn_abi_version(void);
 
 #ifdef __cplusplus

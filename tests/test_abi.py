@@ -42,7 +42,7 @@ def test_status_strings_and_version():
     for code in range(9):
         assert A.attn_status_string(code) not in ("", "unknown status")
     assert A.attn_status_string(99) == "unknown status"
-    assert A.attn_abi_version() == 2
+    assert A.attn_abi_version() == 3
 
 
 def fwd(*, q=P, k=P, v=P, o=P, lse=0, B=1, Hq=32, Hkv=8, Sq=128, Sk=128, D=128, causal=1,
@@ -81,12 +81,12 @@ def test_fwd_empty_problem_is_a_no_op(kw):
 
 
 def dec(*, q=P, kc=P, vc=P, table=P, ctx=P, o=P, lse=0, B=64, Hq=32, Hkv=8, D=128, bs=16,
-        scale=0.08, stride=0, nblocks=0, splits=0, ws=P, ws_bytes=1 << 40, ex=True):
+        scale=0.08, stride=0, nblocks=0, workers=0, ws=P, ws_bytes=1 << 40, ex=True):
     lib = A.load_library()
     if not ex:
         return lib.attn_decode_paged(q, kc, vc, table, ctx, o, B, Hq, Hkv, D, bs, scale, None)
     return lib.attn_decode_paged_ex(q, kc, vc, table, ctx, o, lse, B, Hq, Hkv, D, bs, scale,
-                                    stride, nblocks, splits, ws, ws_bytes, None)
+                                    stride, nblocks, workers, ws, ws_bytes, None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -96,7 +96,7 @@ def dec(*, q=P, kc=P, vc=P, table=P, ctx=P, o=P, lse=0, B=64, Hq=32, Hkv=8, D=12
     (dict(bs=32), UNSUP), (dict(bs=8), UNSUP), (dict(q=P + 8), ALIGN), (dict(kc=P + 4), ALIGN),
     (dict(o=P + 2), ALIGN), (dict(table=P + 2), ALIGN), (dict(ctx=P + 1), ALIGN),
     (dict(lse=P + 2), ALIGN), (dict(scale=NAN), SCALE), (dict(scale=-1.0), SCALE),
-    (dict(splits=65), SHAPE), (dict(splits=-1), SHAPE), (dict(ws_bytes=100), WS),
+    (dict(workers=65537), SHAPE), (dict(workers=-1), SHAPE), (dict(ws_bytes=100), WS),
     (dict(ws=P + 4), WS), (dict(B=70000), SHAPE),
 ])
 def test_decode_rejects(kw, code):
@@ -110,25 +110,31 @@ def test_decode_plain_entry_point_rejects_before_launch():
     assert dec(ex=False, B=0) == OK
 
 
-def test_decode_default_splits():
-    # about 8192 (query head, split) rows per launch, clamped to 1..64
-    assert A.attn_decode_default_splits(64, 32) == 4
-    assert A.attn_decode_default_splits(8, 32) == 32
-    assert A.attn_decode_default_splits(1, 32) == 64
-    assert A.attn_decode_default_splits(1, 1) == 64
-    assert A.attn_decode_default_splits(512, 64) == 1
-    assert A.attn_decode_default_splits(0, 32) == 1
+def test_decode_default_workers():
+    w = A.attn_decode_default_workers()
+    assert 1 <= w <= 65536
+    if "ATTN_DECODE_WORKERS" not in os.environ:
+        assert w % 3 == 0       # three worker waves per compute unit
+
+
+def ws_bytes(B, Hq, Hkv, D, W):
+    g = Hq // Hkv
+    head = (W + B * Hkv) * g * (D + 2) * 4
+    return (head + 15) // 16 * 16 + B * Hkv * 2 * 4
 
 
 def test_decode_workspace_size():
-    d = A.attn_decode_default_splits(64, 32)
-    assert 1 <= d <= 64
-    assert A.attn_decode_workspace_bytes(64, 32, 128, 0) == 64 * 32 * d * 129 * 4
-    assert A.attn_decode_workspace_bytes(3, 5, 64, 7) == 3 * 5 * 7 * 65 * 4
-    assert A.attn_decode_workspace_bytes(1, 1, 64, 65) == 0
-    # exactly the reported size is accepted by the size check (fails later only on launch)
-    need = A.attn_decode_workspace_bytes(64, 32, 128, 4)
-    assert dec(splits=4, ws_bytes=need - 1) == WS
+    w = A.attn_decode_default_workers()
+    assert A.attn_decode_workspace_bytes(64, 32, 8, 128, 0) == ws_bytes(64, 32, 8, 128, w)
+    assert A.attn_decode_workspace_bytes(3, 5, 5, 64, 7) == ws_bytes(3, 5, 5, 64, 7)
+    assert A.attn_decode_workspace_bytes(3, 6, 2, 64, 1) == ws_bytes(3, 6, 2, 64, 1)
+    assert A.attn_decode_workspace_bytes(0, 32, 8, 128, 5) == ws_bytes(0, 32, 8, 128, 5)
+    for bad in [(1, 1, 1, 64, 65537), (1, 1, 1, 64, -1), (1, 6, 4, 64, 1), (1, 1, 1, 80, 1),
+                (-1, 1, 1, 64, 1), (1, 34, 2, 64, 1), (70000, 1, 1, 64, 1)]:
+        assert A.attn_decode_workspace_bytes(*bad) == 0, bad
+    # one byte less than the reported size is refused before anything is launched
+    need = A.attn_decode_workspace_bytes(64, 32, 8, 128, 4)
+    assert dec(workers=4, ws_bytes=need - 1) == WS
 
 
 def test_binding_rejects_cpu_tensors():

@@ -84,11 +84,11 @@ def test_decode_block_permutation_is_bitwise_invariant(dev):
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
-@pytest.mark.parametrize("splits", [1, 2, 3, 8, 64])
-def test_decode_split_count_invariance(splits, dev):
+@pytest.mark.parametrize("workers", [1, 2, 7, 64, 1000, 0, 65536])
+def test_decode_worker_count_invariance(workers, dev):
     d = W.decode_inputs(B=12, Hq=32, Hkv=8, D=128, block_size=16, ctx_lo=1, ctx_hi=2000, seed=6)
     q, kc, vc, bt, cl = upload(d, dev)
-    o, lse = A.attn_decode_paged_ex(q, kc, vc, bt, cl, max_splits=splits)
+    o, lse = A.attn_decode_paged_ex(q, kc, vc, bt, cl, num_workers=workers)
     torch.cuda.synchronize()
     O, L = oracle.decode_paged(d.q, d.k_cache, d.v_cache, d.block_table, d.ctx_lens, 16)
     check_bf16(to_np(o), O)
@@ -142,9 +142,9 @@ def test_decode_zero_context_and_caller_workspace(dev):
     d = W.decode_inputs(B=4, Hq=8, Hkv=2, D=64, block_size=16, ctx_lo=1, ctx_hi=100, seed=9,
                         ctx_lens=[0, 50, 0, 17])
     q, kc, vc, bt, cl = upload(d, dev)
-    nbytes = A.attn_decode_workspace_bytes(4, 8, 64, 4)
+    nbytes = A.attn_decode_workspace_bytes(4, 8, 2, 64, 4)
     ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-    o, lse = A.attn_decode_paged_ex(q, kc, vc, bt, cl, max_splits=4, workspace=ws)
+    o, lse = A.attn_decode_paged_ex(q, kc, vc, bt, cl, num_workers=4, workspace=ws)
     torch.cuda.synchronize()
     O, L = oracle.decode_paged(d.q, d.k_cache, d.v_cache, d.block_table, d.ctx_lens, 16)
     check_bf16(to_np(o), O)

@@ -7,7 +7,10 @@ One step is one pass of the whole hot path over one batch of synthetic input:
   * decode:  attn_decode_paged on the paged workload (B=64, Hq=32, Hkv=8, D=128, contexts
     uniform in [512, 4096], 16-token blocks placed by a seeded permutation), which runs the
     split-KV stream kernel and the LSE-merge combine kernel.
-Inputs are generated once, uploaded, and resident in HBM before timing starts.
+Inputs are generated once, uploaded, and resident in HBM before timing starts. Between the two,
+512 MiB of scratch memory is read (``--flush-mib``), so the decode starts with none of its K/V in
+L2 or the memory-side cache; the flush is outside both kernels' timed intervals but inside the
+step's wall time (``ms_per_step``).
 
 Printed (one JSON line): ``value`` is the prefill kernel's throughput in TFLOP/s counting
 4*D flops per visible (query, key) pair (causal-adjusted); ``decode`` gives the decode KV
@@ -155,6 +158,55 @@ def cpu_baseline(min_seconds: float):
                       f"{os.cpu_count()}, affinity {len(os.sched_getaffinity(0))}"}
 
 
+def decode_graph_timing(A, torch, dq, dkc, dvc, dbt, dctx, scale, stream, reps):
+    """The decode (stream + combine kernels) captured once into a hipGraph through
+    attn_decode_paged_ex with a caller workspace, then replayed back to back: GPU time per
+    replay (events around all replays) and host time per enqueue, against the same number of
+    eager calls through the Python binding."""
+    B, Hq, D = dq.shape
+    Hkv = dkc.shape[1]
+    ws = torch.empty(A.attn_decode_workspace_bytes(B, Hq, Hkv, D, 0), dtype=torch.uint8,
+                     device=dq.device)
+    out = torch.empty_like(dq)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=dq.device)
+
+    def call():
+        A.attn_decode_paged_ex(dq, dkc, dvc, dbt, dctx, scale=scale, out=out, lse=lse,
+                               workspace=ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    torch.cuda.synchronize()
+    ev = HipEvents(4)
+    res = {}
+    for name, fn in (("eager", call), ("graph", g.replay)):
+        fn()
+        torch.cuda.synchronize()
+        ev.record(2 * (name == "graph"), stream)
+        h0 = time.perf_counter()
+        for _ in range(reps):
+            fn()
+        h1 = time.perf_counter()
+        ev.record(2 * (name == "graph") + 1, stream)
+        torch.cuda.synchronize()
+        res[name] = (ev.elapsed_ms(2 * (name == "graph"), 2 * (name == "graph") + 1) * 1e3 / reps,
+                     (h1 - h0) * 1e6 / reps)
+    ev.close()
+    return {"replays": reps,
+            "gpu_us_per_call_eager": round(res["eager"][0], 2),
+            "gpu_us_per_call_graph": round(res["graph"][0], 2),
+            "host_us_per_enqueue_eager": round(res["eager"][1], 2),
+            "host_us_per_enqueue_graph": round(res["graph"][1], 2),
+            "note": "back to back, no cache flush in between"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -162,6 +214,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum host time for the oracle baseline (0 skips it)")
+    ap.add_argument("--graph-reps", type=int, default=50,
+                    help="replays of the decode captured in a hipGraph (0 = skip that part)")
+    ap.add_argument("--flush-mib", type=int, default=512,
+                    help="scratch MiB read before each decode, outside its timing "
+                         "(0 = none)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this size (for counter scaling)")
     args = ap.parse_args()
@@ -194,16 +251,29 @@ def main():
 
     stream = torch.cuda.current_stream().cuda_stream
 
+    # Read once before every decode, outside its timed interval: 512 MiB is twice the MI355X's
+    # 256 MiB memory-side cache, so the decode finds none of its 624 MB of K/V left in a cache
+    # by the previous step (a serving loop runs other layers in between). A read, not a write:
+    # written scratch would leave dirty lines whose write-back then lands inside the decode.
+    flush = torch.zeros((args.flush_mib << 20) // 4, dtype=torch.int32, device=dev) \
+        if args.flush_mib > 0 else None
+    flush_sink = torch.zeros(1, dtype=torch.int64, device=dev)
+
     def step(i=None):
-        # events i0 | prefill | i1 | decode (split + combine) | i2, all on the launch stream
+        # events e0 | prefill | e1 | cache flush | e2 | decode (stream + combine) | e3, all on
+        # the launch stream
         if i is not None:
-            ev.record(3 * i, stream)
+            ev.record(4 * i, stream)
         A.attn_fwd(qg, kg, vg, causal=True, scale=scale_p, out=o, lse=lse)
         if i is not None:
-            ev.record(3 * i + 1, stream)
+            ev.record(4 * i + 1, stream)
+        if flush is not None:
+            torch.sum(flush, dim=0, dtype=torch.int64, out=flush_sink[0])
+        if i is not None:
+            ev.record(4 * i + 2, stream)
         A.attn_decode_paged(dq, dkc, dvc, dbt, dctx, scale=scale_d, out=do)
         if i is not None:
-            ev.record(3 * i + 2, stream)
+            ev.record(4 * i + 3, stream)
 
     if args.calibrate_copy_mib > 0:
         n = args.calibrate_copy_mib << 20
@@ -216,7 +286,7 @@ def main():
 
     for _ in range(args.warmup):
         step()
-    ev = HipEvents(3 * args.steps)
+    ev = HipEvents(4 * args.steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -224,9 +294,11 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
 
-    fwd_ms = float(np.mean([ev.elapsed_ms(3 * i, 3 * i + 1) for i in range(args.steps)]))
-    dec_ms = float(np.mean([ev.elapsed_ms(3 * i + 1, 3 * i + 2) for i in range(args.steps)]))
+    fwd_ms = float(np.mean([ev.elapsed_ms(4 * i, 4 * i + 1) for i in range(args.steps)]))
+    dec_ms = float(np.mean([ev.elapsed_ms(4 * i + 2, 4 * i + 3) for i in range(args.steps)]))
     ev.close()
+    graph = decode_graph_timing(A, torch, dq, dkc, dvc, dbt, dctx, scale_d, stream,
+                                args.graph_reps) if args.graph_reps > 0 else None
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     flops = prefill_flops(PREFILL)
     tflops = flops / (fwd_ms * 1e-3) / 1e12
@@ -255,6 +327,7 @@ def main():
             "prefill_flops_per_launch": flops,
             "decode_bytes_per_launch": dbytes,
             "sum_ctx": int(np.sum(ctx_lens)),
+            "cache_flush_mib_before_decode": args.flush_mib,
         },
         "prefill": {"kernel_ms": round(fwd_ms, 5), "tflops": round(tflops, 2),
                     "frac_of_peak": round(tflops / PEAK_BF16_TFLOPS, 4)},
@@ -269,6 +342,8 @@ def main():
                      "traffic": measured_traffic("fwd_bf16_llama3_8b_prefill", fwd_digest)},
         "kernel_source_digest": {"fwd": fwd_digest, "decode": dec_digest},
     }
+    if graph is not None:
+        out["decode"]["hipgraph"] = graph
     if args.cpu_seconds > 0:
         out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -14,7 +14,10 @@ Sources of the facts:
     closed form and printed to ten digits);
   * exactness up to rounding order: "Kernel Fusion, Softmax, and Attention", fifth paragraph;
   * the paged cache with a block table: "Optimizing Large Language Model Inference ...",
-    §Paged Attention and Dynamic KV Cache Management.
+    §Paged Attention and Dynamic KV Cache Management;
+  * the residual add + RMS norm and its two outputs: "Kernel and Operator Fusion -- Inference
+    Optimization", §4 (the unfused listing: add, mean of squares, reciprocal square root of
+    that plus eps, times the weight) and §5 (the new residual is returned too).
 """
 from __future__ import annotations
 
@@ -24,6 +27,7 @@ from decimal import Decimal, getcontext
 import numpy as np
 
 import oracle.direct as OA
+import oracle.rmsnorm as ON
 
 
 def _fwd(*a, **kw):
@@ -32,6 +36,10 @@ def _fwd(*a, **kw):
 
 def _dec(*a, **kw):
     return OA.decode_paged(*a, **kw)
+
+
+def _norm(*a, **kw):
+    return ON.add_rms_norm(*a, **kw)
 
 
 def _rng(seed):
@@ -415,9 +423,83 @@ def pin_decode_paged():
         _close(L3, L, 0.0, "poisoned tail LSE")
 
 
+# --- N4: residual add + RMS norm ---------------------------------------------------------
+def _norm_rows(seed, M=4, d=37):
+    rng = _rng(seed)
+    x = rng.standard_normal((M, d)).astype(np.float32)
+    r = rng.standard_normal((M, d)).astype(np.float32)
+    w = (1.0 + 0.1 * rng.standard_normal(d)).astype(np.float32)
+    return x, r, w
+
+
+def pin_norm_residual_is_sum():
+    """The second output is the sum x + residual itself (the page returns it for the next
+    layer's add), exactly: the sum of two float32 values is exact in float64."""
+    x, r, w = _norm_rows(40)
+    _, t = _norm(x, r, w)
+    assert np.array_equal(t, x.astype(np.float64) + r.astype(np.float64))
+    assert np.array_equal(_norm(r, x, w)[1], t)           # the add is symmetric
+
+
+def pin_norm_unit_rms():
+    """With eps = 0 and unit weight, every output row has mean square exactly 1: the row is
+    divided by the root of its mean square (the mean over d, not the sum or d - 1)."""
+    x, r, _ = _norm_rows(41, M=6, d=29)
+    out, _ = _norm(x, r, np.ones(29, np.float32), eps=0.0)
+    ms = np.mean(out * out, axis=1)
+    _close(ms, np.ones(6), 1e-13, "mean square of the normalised rows")
+
+
+def pin_norm_scale_invariance():
+    """eps = 0: scaling x and the residual by the same a > 0 leaves the output unchanged (the
+    normalisation divides the scale out); scaling the weight scales the output."""
+    x, r, w = _norm_rows(42)
+    o1, _ = _norm(x, r, w, eps=0.0)
+    o2, _ = _norm(3.75 * x.astype(np.float64), 3.75 * r.astype(np.float64), w, eps=0.0)
+    _close(o2, o1, 1e-13, "scale invariance")
+    o3, _ = _norm(x, r, 2.0 * w.astype(np.float64), eps=0.0)
+    _close(o3, 2.0 * o1, 1e-13, "linear in the weight")
+    o4, _ = _norm(-x.astype(np.float64), -r.astype(np.float64), w, eps=0.0)
+    _close(o4, -o1, 1e-13, "odd in the input")
+
+
+def pin_norm_constant_and_eps():
+    """Closed forms that fix where eps enters: a row whose sum is the constant c gives
+    c / sqrt(c^2 + eps) * w. With c^2 = eps the result is w / sqrt(2) exactly; with eps = 0
+    it is sign(c) * w."""
+    d = 8
+    w = np.linspace(0.5, 1.5, d)
+    c = 1e-3                                   # c^2 = 1e-6 = eps
+    x = np.full((1, d), c / 4)
+    r = np.full((1, d), 3 * c / 4)
+    out, _ = _norm(x, r, w, eps=1e-6)
+    _close(out[0], w / math.sqrt(2.0), 1e-12, "constant row with c^2 = eps")
+    out0, _ = _norm(-x, -r, w, eps=0.0)
+    _close(out0[0], -w, 1e-12, "constant row, eps = 0")
+    big, _ = _norm(1e3 * x, 1e3 * r, w, eps=1e-6)      # c = 1: eps nearly negligible
+    _close(big[0], w / math.sqrt(1.0 + 1e-6), 1e-12, "constant row with c = 1")
+
+
+def pin_norm_brute_force():
+    """Scalar Decimal arithmetic (40 digits) straight from the page's unfused listing, on
+    small rows, independent of numpy."""
+    getcontext().prec = 40
+    x, r, w = _norm_rows(43, M=2, d=5)
+    out, t = _norm(x, r, w, eps=1e-6)
+    for i in range(2):
+        ti = [Decimal(float(x[i, j])) + Decimal(float(r[i, j])) for j in range(5)]
+        var = sum(v * v for v in ti) / Decimal(5)
+        inv = Decimal(1) / (var + Decimal("0.000001")).sqrt()
+        for j in range(5):
+            ref = ti[j] * inv * Decimal(float(w[j]))
+            assert abs(Decimal(float(out[i, j])) - ref) <= Decimal("1e-13"), (i, j)
+            assert Decimal(float(t[i, j])) == ti[j]
+
+
 ALL_PINS = [
     pin_rows_sum_to_one, pin_worked_row, pin_online_equals_two_pass, pin_split_merge,
     pin_stability, pin_masked_row, pin_identical_keys, pin_causal_row0, pin_degenerate,
     pin_brute_force, pin_shift_invariance, pin_v_affine, pin_gqa, pin_permutations,
-    pin_decode_paged,
+    pin_decode_paged, pin_norm_residual_is_sum, pin_norm_unit_rms, pin_norm_scale_invariance,
+    pin_norm_constant_and_eps, pin_norm_brute_force,
 ]

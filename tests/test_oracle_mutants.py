@@ -7,6 +7,7 @@ import numpy as np
 import pytest
 
 import oracle.direct as OA
+import oracle.rmsnorm as ON
 from tests import pins
 
 
@@ -142,3 +143,53 @@ def test_gqa_mutant_is_caught(monkeypatch):
 def test_gather_mutant_is_caught(kind, monkeypatch):
     monkeypatch.setattr(OA, "gather_paged", _gather_mutant(kind))
     assert "pin_decode_paged" in _some_pin_fails()
+
+
+def _norm_mutant(kind):
+    def add_rms_norm(x, residual, weight, eps=1e-6):
+        x = np.asarray(x, dtype=np.float64)
+        r = np.asarray(residual, dtype=np.float64)
+        w = np.asarray(weight, dtype=np.float64)
+        t = x - r if kind == "residual_sub" else x + r
+        d = t.shape[-1]
+        if kind == "sum_not_mean":
+            ms = np.sum(t * t, axis=-1, keepdims=True)
+        elif kind == "d_minus_1":
+            ms = np.sum(t * t, axis=-1, keepdims=True) / (d - 1)
+        elif kind == "centred":
+            ms = np.var(t, axis=-1, keepdims=True)
+        else:
+            ms = np.mean(t * t, axis=-1, keepdims=True)
+        if kind == "no_eps":
+            inv = 1.0 / np.sqrt(ms)
+        elif kind == "eps_outside":
+            inv = 1.0 / np.sqrt(ms) + eps
+        elif kind == "no_sqrt":
+            inv = 1.0 / (ms + eps)
+        else:
+            inv = 1.0 / np.sqrt(ms + eps)
+        out = t * inv
+        if kind == "weight_added":
+            out = out + w
+        elif kind != "no_weight":
+            out = out * w
+        if kind == "returns_input":
+            return out, x
+        return out, t
+    return add_rms_norm
+
+
+NORM_MUTANTS = ["residual_sub", "sum_not_mean", "d_minus_1", "centred", "no_eps",
+                "eps_outside", "no_sqrt", "weight_added", "no_weight", "returns_input"]
+
+
+@pytest.mark.parametrize("kind", NORM_MUTANTS)
+def test_norm_mutant_is_caught(kind, monkeypatch):
+    monkeypatch.setattr(ON, "add_rms_norm", _norm_mutant(kind))
+    failed = [f for f in _some_pin_fails() if f.startswith("pin_norm")]
+    assert failed, f"no pin catches mutant {kind}"
+
+
+def test_unmutated_norm_copy_passes(monkeypatch):
+    monkeypatch.setattr(ON, "add_rms_norm", _norm_mutant("none"))
+    assert _some_pin_fails() == []

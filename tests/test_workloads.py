@@ -96,3 +96,22 @@ def test_sample_rows_cover_edges():
     rows = W.sample_rows(2, 4, 100, 20, seed=1, must=(63, 64, 99))
     assert len(rows) == 20 and (0, 0, 0) in rows and (1, 3, 99) in rows
     assert {63, 64}.issubset({i for _, _, i in rows})
+
+
+def test_norm_inputs_are_bf16_exact_and_seeded():
+    x, r, w = W.norm_inputs(5, 24, seed=3)
+    assert x.shape == (5, 24) and r.shape == (5, 24) and w.shape == (24,)
+    for a in (x, r, w):
+        assert a.dtype == np.float32
+        assert np.array_equal(W.bf16_round(a), a)
+    x2, r2, w2 = W.norm_inputs(5, 24, seed=3)
+    assert np.array_equal(x, x2) and np.array_equal(r, r2) and np.array_equal(w, w2)
+    assert abs(float(w.mean()) - 1.0) < 0.2
+    cfg = W.NORM_CONFIGS["add_rms_norm_64x8192"]
+    assert (cfg.M, cfg.d, cfg.eps) == (64, 8192, 1e-6)
+
+
+def test_norm_workload_is_the_pages_tensor():
+    it = _golden()["add_rms_norm_tensor"]
+    c = W.NORM_CONFIGS["add_rms_norm_64x8192"]
+    assert (c.M, c.d, c.eps) == (it["M"], it["d"], it["eps"]) and it["dtype"] == "bf16"

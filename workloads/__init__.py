@@ -16,7 +16,11 @@ Workload shapes follow the pages:
     Management", §FlashAttention and the Memory-Efficiency Revolution;
   * the paged decode layout (fixed-size blocks, a block table mapping a sequence's logical
     blocks to physical ones) is the one in §Paged Attention and Dynamic KV Cache Management
-    of that same article.
+    of that same article;
+  * the residual-add RMS norm is measured on a (64, 8192) bfloat16 tensor in "Kernel and
+    Operator Fusion -- Inference Optimization", §4; the other two shapes are the Llama-3-8B
+    hidden width (4096, the projection input width of §5) over a 2048-token prefill, and an
+    8192-wide hidden state over 16384 tokens for a bandwidth-bound size.
 """
 from __future__ import annotations
 
@@ -27,7 +31,8 @@ import numpy as np
 
 __all__ = [
     "FwdConfig", "DecodeConfig", "CONFIGS", "bf16_round", "bf16_bits", "bits_to_f32",
-    "fwd_inputs", "decode_inputs", "DecodeInputs", "sample_rows",
+    "fwd_inputs", "decode_inputs", "DecodeInputs", "sample_rows", "NormConfig", "NORM_CONFIGS",
+    "norm_inputs", "norm_inputs_for",
 ]
 
 
@@ -221,3 +226,39 @@ def sample_rows(B, Hq, Sq, n, seed, must=()):
     while len(picks) < n:
         picks.add((int(rng.integers(B)), int(rng.integers(Hq)), int(rng.integers(Sq))))
     return sorted(picks)
+
+
+# ----------------------------------------------------------------------------------------
+# Residual-add RMS norm inputs
+# ----------------------------------------------------------------------------------------
+@dataclass(frozen=True)
+class NormConfig:
+    name: str
+    M: int          # rows (tokens)
+    d: int          # row length (hidden size)
+    seed: int
+    eps: float = 1e-6
+    kind: str = "norm"
+
+
+NORM_CONFIGS = {
+    "add_rms_norm_64x8192": NormConfig("add_rms_norm_64x8192", M=64, d=8192, seed=1006),
+    "add_rms_norm_2048x4096": NormConfig("add_rms_norm_2048x4096", M=2048, d=4096, seed=1007),
+    "add_rms_norm_16384x8192": NormConfig("add_rms_norm_16384x8192", M=16384, d=8192,
+                                          seed=1008),
+}
+
+
+def norm_inputs(M, d, seed):
+    """x and residual [M, d] ~ N(0, 1) and weight [d] ~ 1 + 0.1 N(0, 1), drawn in that order
+    and rounded to bfloat16 (returned as exact float32 arrays)."""
+    rng = np.random.default_rng(seed)
+    x = bf16_round(rng.standard_normal(size=(M, d), dtype=np.float32))
+    r = bf16_round(rng.standard_normal(size=(M, d), dtype=np.float32))
+    w = bf16_round(np.float32(1.0) + np.float32(0.1) * rng.standard_normal(size=d,
+                                                                          dtype=np.float32))
+    return x, r, w
+
+
+def norm_inputs_for(cfg: NormConfig):
+    return norm_inputs(cfg.M, cfg.d, cfg.seed)

@@ -158,6 +158,40 @@ def cpu_baseline(min_seconds: float):
                       f"{os.cpu_count()}, affinity {len(os.sched_getaffinity(0))}"}
 
 
+def norm_timing(A, torch, dev, flush, flush_sink, stream, reps):
+    """The fused residual-add RMS norm on the page's (64, 8192) bf16 tensor and on an
+    8192-wide hidden state over 16384 tokens. Each launch is timed alone with fence-free
+    events, after the same 512 MiB read flush as the decode. Algorithmic bytes: x and the
+    residual read, out and the new residual written (8 B per element) plus the weight row."""
+    res = {}
+    for name in ("add_rms_norm_64x8192", "add_rms_norm_16384x8192"):
+        cfg = W.NORM_CONFIGS[name]
+        x, r, w = W.norm_inputs_for(cfg)
+        gx = torch.from_numpy(x).to(dev).to(torch.bfloat16)
+        gr = torch.from_numpy(r).to(dev).to(torch.bfloat16)
+        gw = torch.from_numpy(w).to(dev).to(torch.bfloat16)
+        del x, r, w
+        out, tres = torch.empty_like(gx), torch.empty_like(gx)
+        A.add_rms_norm(gx, gr, gw, eps=cfg.eps, out=out, residual_out=tres)
+        torch.cuda.synchronize()
+        ev = HipEvents(2 * reps)
+        for i in range(reps):
+            if flush is not None:
+                torch.sum(flush, dim=0, dtype=torch.int64, out=flush_sink[0])
+            ev.record(2 * i, stream)
+            A.add_rms_norm(gx, gr, gw, eps=cfg.eps, out=out, residual_out=tres)
+            ev.record(2 * i + 1, stream)
+        torch.cuda.synchronize()
+        us = float(np.median([ev.elapsed_ms(2 * i, 2 * i + 1) for i in range(reps)])) * 1e3
+        ev.close()
+        nbytes = 8.0 * cfg.M * cfg.d + 2.0 * cfg.d
+        gbs = nbytes / (us * 1e-6) / 1e9
+        res[name] = {"us": round(us, 2), "bytes_per_launch": nbytes, "GB/s": round(gbs, 1),
+                     "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
+        del gx, gr, gw, out, tres
+    return res
+
+
 def decode_graph_timing(A, torch, dq, dkc, dvc, dbt, dctx, scale, stream, reps):
     """The decode (stream + combine kernels) captured once into a hipGraph through
     attn_decode_paged_ex with a caller workspace, then replayed back to back: GPU time per
@@ -214,6 +248,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum host time for the oracle baseline (0 skips it)")
+    ap.add_argument("--norm-reps", type=int, default=20,
+                    help="timed launches of the fused add_rms_norm per shape (0 = skip)")
     ap.add_argument("--graph-reps", type=int, default=50,
                     help="replays of the decode captured in a hipGraph (0 = skip that part)")
     ap.add_argument("--flush-mib", type=int, default=512,
@@ -299,6 +335,8 @@ def main():
     ev.close()
     graph = decode_graph_timing(A, torch, dq, dkc, dvc, dbt, dctx, scale_d, stream,
                                 args.graph_reps) if args.graph_reps > 0 else None
+    norm = norm_timing(A, torch, dev, flush, flush_sink, stream, args.norm_reps) \
+        if args.norm_reps > 0 else None
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     flops = prefill_flops(PREFILL)
     tflops = flops / (fwd_ms * 1e-3) / 1e12
@@ -344,6 +382,8 @@ def main():
     }
     if graph is not None:
         out["decode"]["hipgraph"] = graph
+    if norm is not None:
+        out["add_rms_norm"] = norm
     if args.cpu_seconds > 0:
         out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -18,7 +18,8 @@ __all__ = [
     "AttnError", "library_path", "load_library",
     "attn_fwd", "attn_fwd_f32", "attn_decode_paged", "attn_decode_paged_ex",
     "attn_decode_workspace_bytes", "attn_decode_default_workers", "attn_status_string",
-    "attn_last_error", "attn_release_workspace", "attn_abi_version", "EXPORTED_SYMBOLS",
+    "attn_last_error", "attn_release_workspace", "attn_abi_version", "attn_add_rms_norm",
+    "add_rms_norm", "EXPORTED_SYMBOLS",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -38,6 +39,7 @@ _SIGNATURES = {
     "attn_last_error": (ctypes.c_char_p, []),
     "attn_release_workspace": (None, []),
     "attn_abi_version": (_I, []),
+    "attn_add_rms_norm": (_I, [_P, _P, _P, _P, _P, _I, _I, _F, _P]),
 }
 EXPORTED_SYMBOLS = tuple(_SIGNATURES)
 
@@ -258,3 +260,35 @@ def attn_decode_paged_ex(q, k_cache, v_cache, block_table, ctx_lens, scale=None,
             int(nb) if check_blocks else 0, int(num_workers), _ptr(workspace),
             int(workspace.numel()) if workspace is not None else 0, _stream_ptr(dev, stream)))
     return out, lse
+
+
+def add_rms_norm(x, residual, weight, eps=1e-6, out=None, residual_out=None, stream=None):
+    """Fused residual add + RMS norm (bf16): returns (out, residual_out) with
+    residual_out = x + residual and out = residual_out * rsqrt(mean(residual_out^2) + eps) *
+    weight over the last dimension. x and residual are [..., d], weight [d]. Pass out=x and/or
+    residual_out=residual to work in place."""
+    torch = _torch()
+    if x.dim() < 1 or tuple(residual.shape) != tuple(x.shape):
+        raise ValueError(f"x {tuple(x.shape)} and residual {tuple(residual.shape)} must match")
+    d = x.shape[-1]
+    M = x.numel() // d if d else 0
+    dev = x.device
+    _need(x, "x", torch.bfloat16, dev)
+    _need(residual, "residual", torch.bfloat16, dev)
+    _need(weight, "weight", torch.bfloat16, dev, (d,))
+    if out is None:
+        out = torch.empty_like(x)
+    if residual_out is None:
+        residual_out = torch.empty_like(x)
+    _need(out, "out", torch.bfloat16, dev, tuple(x.shape))
+    _need(residual_out, "residual_out", torch.bfloat16, dev, tuple(x.shape))
+    with torch.cuda.device(dev):
+        _check(load_library().attn_add_rms_norm(
+            _ptr(x), _ptr(residual), _ptr(weight), _ptr(out), _ptr(residual_out), int(M), int(d),
+            float(eps), _stream_ptr(dev, stream)))
+    return out, residual_out
+
+
+def attn_add_rms_norm(*args, **kw):
+    """Alias of :func:`add_rms_norm` under the C symbol's name."""
+    return add_rms_norm(*args, **kw)

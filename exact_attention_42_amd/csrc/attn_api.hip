@@ -195,9 +195,34 @@ int run_decode(const void* q, const void* k_cache, const void* v_cache,
   return ok();
 }
 
+int run_add_rms_norm(const void* x, const void* residual, const void* weight, void* out,
+                     void* residual_out, int M, int d, float eps, void* stream) {
+  if (M < 0 || d < 0) return fail(ATTN_ERR_SHAPE, "M and d must be >= 0 (M=%d d=%d)", M, d);
+  if (d == 0 || d % 8 != 0 || d > 65536)
+    return fail(ATTN_ERR_UNSUPPORTED, "row length d=%d not supported (a multiple of 8, 8..65536)",
+                d);
+  if (!std::isfinite(eps) || eps < 0.f)
+    return fail(ATTN_ERR_SCALE, "eps must be finite and >= 0 (got %g)", (double)eps);
+  if (M == 0) return ok();
+  if (!x || !residual || !weight || !out || !residual_out)
+    return fail(ATTN_ERR_NULL, "x, residual, weight, out and residual_out must not be NULL");
+  if (!aligned(x, 16) || !aligned(residual, 16) || !aligned(weight, 16) || !aligned(out, 16) ||
+      !aligned(residual_out, 16))
+    return fail(ATTN_ERR_ALIGN, "x, residual, weight, out and residual_out must be 16-byte aligned");
+  attn::NormProblem p{x, residual, weight, out, residual_out, M, d, eps};
+  hipError_t e = attn::launch_add_rms_norm(p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "attn_add_rms_norm launch");
+  return ok();
+}
+
 }  // namespace
 
 extern "C" {
+
+int attn_add_rms_norm(const void* x, const void* residual, const void* weight, void* out,
+                      void* residual_out, int M, int d, float eps, void* stream) {
+  return run_add_rms_norm(x, residual, weight, out, residual_out, M, d, eps, stream);
+}
 
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
              int Hkv, int Sq, int Sk, int D, int causal, float scale, void* stream) {
@@ -266,6 +291,6 @@ void attn_release_workspace(void) {
   if (have_cur) (void)hipSetDevice(cur);
 }
 
-int attn_abi_version(void) { return 3; }
+int attn_abi_version(void) { return 4; }
 
 }  // extern "C"

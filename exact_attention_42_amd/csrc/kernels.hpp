@@ -44,4 +44,18 @@ struct DecodeProblem {
 size_t decode_workspace_bytes(int B, int Hkv, int group, int D, int workers);
 hipError_t launch_decode_paged(const DecodeProblem& p, hipStream_t stream);
 
+struct NormProblem {
+  const void* x;            // [M, d] bf16
+  const void* residual;     // [M, d] bf16
+  const void* weight;       // [d] bf16
+  void* out;                // [M, d] bf16 (may be x)
+  void* residual_out;       // [M, d] bf16 (may be residual)
+  int M, d;                 // d a multiple of 8, 8 <= d <= 65536
+  float eps;
+};
+
+// Threads per row the residual-add RMS norm launches for a row of d elements.
+int add_rms_norm_threads(int d);
+hipError_t launch_add_rms_norm(const NormProblem& p, hipStream_t stream);
+
 }  // namespace attn

@@ -117,6 +117,26 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int D, int num_worker
  * variable ATTN_DECODE_WORKERS = 1..65536 overrides it. */
 int attn_decode_default_workers(void);
 
+/* Fused residual add + RMS normalisation of M rows of d elements ("Kernel and Operator
+ * Fusion -- Inference Optimization", §4 Tiny example, §5 Why add_rms_norm returns two
+ * things): per row,
+ *   residual_out = x + residual
+ *   out          = residual_out * rsqrt(mean(residual_out^2) + eps) * weight
+ * with the mean over the row's d elements.
+ *   x, residual:        [M, d] bf16, row-major, read only (unless aliased below)
+ *   weight:             [d] bf16
+ *   out, residual_out:  [M, d] bf16, written. out may be the same buffer as x and
+ *                       residual_out the same buffer as residual (in place); any other
+ *                       overlap is undefined.
+ * The add, the sum of squares and the scaling are done in fp32; residual_out and out are
+ * rounded to bf16 (nearest even) once, at their stores.
+ * Requirements: d a multiple of 8 with 8 <= d <= 65536 (else ATTN_ERR_UNSUPPORTED); M >= 0
+ * (M == 0 is a no-op); all pointers non-NULL (ATTN_ERR_NULL) and 16-byte aligned
+ * (ATTN_ERR_ALIGN); eps finite and >= 0 (ATTN_ERR_SCALE). One kernel on stream, no
+ * synchronisation; the caller owns every buffer. */
+int attn_add_rms_norm(const void* x, const void* residual, const void* weight, void* out,
+                      void* residual_out, int M, int d, float eps, void* stream);
+
 /* Static text for a status code. */
 const char* attn_status_string(int status);
 
@@ -126,7 +146,7 @@ const char* attn_last_error(void);
 /* Frees the library-owned decode workspaces (synchronises the devices that hold them). */
 void attn_release_workspace(void);
 
-/* ABI version of this header: 3. */
+/* ABI version of this header: 4. */
 int attn_abi_version(void);
 
 #ifdef __cplusplus

@@ -42,7 +42,7 @@ def test_status_strings_and_version():
     for code in range(9):
         assert A.attn_status_string(code) not in ("", "unknown status")
     assert A.attn_status_string(99) == "unknown status"
-    assert A.attn_abi_version() == 3
+    assert A.attn_abi_version() == 4
 
 
 def fwd(*, q=P, k=P, v=P, o=P, lse=0, B=1, Hq=32, Hkv=8, Sq=128, Sk=128, D=128, causal=1,
@@ -157,3 +157,33 @@ def test_library_defines_every_kernel_launch_stub():
                          check=True).stdout
     undefined = [l for l in out.splitlines() if " U " in l and "device_stub" in l]
     assert undefined == []
+
+
+def norm(*, x=P, r=P, w=P, o=P, t=P, M=4, d=4096, eps=1e-6):
+    return A.load_library().attn_add_rms_norm(x, r, w, o, t, M, d, eps, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=0), NULL), (dict(r=0), NULL), (dict(w=0), NULL), (dict(o=0), NULL),
+    (dict(t=0), NULL), (dict(M=-1), SHAPE), (dict(d=-8), SHAPE), (dict(d=0), UNSUP),
+    (dict(d=12), UNSUP), (dict(d=65544), UNSUP), (dict(eps=NAN), SCALE),
+    (dict(eps=-1e-6), SCALE), (dict(eps=float("inf")), SCALE), (dict(x=P + 8), ALIGN),
+    (dict(t=P + 2), ALIGN), (dict(w=P + 4), ALIGN),
+])
+def test_norm_rejects(kw, code):
+    assert norm(**kw) == code
+    assert A.attn_last_error() != ""
+
+
+def test_norm_empty_is_a_no_op():
+    assert norm(M=0, x=0, r=0, w=0, o=0, t=0) == OK
+    assert A.attn_last_error() == ""
+
+
+def test_norm_binding_checks_shapes():
+    torch = pytest.importorskip("torch")
+    x = torch.zeros(2, 16, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        A.add_rms_norm(x, x, torch.zeros(16, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="must match"):
+        A.add_rms_norm(x, torch.zeros(2, 8, dtype=torch.bfloat16), x[0])

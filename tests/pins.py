@@ -17,7 +17,11 @@ Sources of the facts:
     §Paged Attention and Dynamic KV Cache Management;
   * the residual add + RMS norm and its two outputs: "Kernel and Operator Fusion -- Inference
     Optimization", §4 (the unfused listing: add, mean of squares, reciprocal square root of
-    that plus eps, times the weight) and §5 (the new residual is returned too).
+    that plus eps, times the weight) and §5 (the new residual is returned too);
+  * RoPE then the KV store, fused ("Kernel and Operator Fusion -- Inference Optimization",
+    §2 item 6): the pages give no formula, so the pins fix the reading taken (rotate-half
+    pairs, theta_i = base^(-2i/D)) by a hand-worked vector, and the properties any rotary
+    embedding has (norm kept, positions compose, scores depend only on relative position).
 """
 from __future__ import annotations
 
@@ -28,6 +32,7 @@ import numpy as np
 
 import oracle.direct as OA
 import oracle.rmsnorm as ON
+import oracle.rotary as OR
 
 
 def _fwd(*a, **kw):
@@ -40,6 +45,14 @@ def _dec(*a, **kw):
 
 def _norm(*a, **kw):
     return ON.add_rms_norm(*a, **kw)
+
+
+def _rope(*a, **kw):
+    return OR.rope(*a, **kw)
+
+
+def _rope_write(*a, **kw):
+    return OR.rope_cache_write(*a, **kw)
 
 
 def _rng(seed):
@@ -496,10 +509,75 @@ def pin_norm_brute_force():
             assert Decimal(float(t[i, j])) == ti[j]
 
 
+# --- N1: rotary embedding + paged cache write ---------------------------------------------
+def pin_rope_worked():
+    """D = 4, base 10000, position 1: pairs (0, 2) turn by 1 rad and (1, 3) by 10000^-1/2 =
+    0.01 rad; written out with scalar math.cos / math.sin."""
+    y = _rope(np.array([[[1.0, 2.0, 3.0, 4.0]]]), [1], base=10000.0)[0, 0]
+    c1, s1, c2, s2 = math.cos(1.0), math.sin(1.0), math.cos(0.01), math.sin(0.01)
+    ref = [1 * c1 - 3 * s1, 2 * c2 - 4 * s2, 3 * c1 + 1 * s1, 4 * c2 + 2 * s2]
+    _close(y, ref, 1e-14, "worked rotary vector")
+    # position 0 is the identity; D = 2 turns the single pair by p radians
+    x = _rng(50).standard_normal((3, 2, 8))
+    _close(_rope(x, [0, 0, 0]), x, 0.0, "position 0")
+    y2 = _rope(np.array([[[0.6, -0.8]]]), [3])[0, 0]
+    _close(y2, [0.6 * math.cos(3) + 0.8 * math.sin(3), -0.8 * math.cos(3) + 0.6 * math.sin(3)],
+           1e-14, "D = 2")
+
+
+def pin_rope_rotation_properties():
+    """Each pair is rotated: head-vector norms are kept, rotations by a and b compose to a + b,
+    and a query-key score depends only on the distance between the positions."""
+    rng = _rng(51)
+    x = rng.standard_normal((5, 3, 16))
+    pos = np.array([0, 1, 7, 100, 4095])
+    y = _rope(x, pos)
+    _close(np.linalg.norm(y, axis=-1), np.linalg.norm(x, axis=-1), 1e-12, "norm kept")
+    _close(_rope(_rope(x, pos, base=500.0), 2 * pos + 3, base=500.0), _rope(x, 3 * pos + 3,
+           base=500.0), 1e-10, "composition")
+    q = rng.standard_normal((1, 1, 16))
+    k = rng.standard_normal((1, 1, 16))
+    for m, n, sh in ((5, 2, 40), (0, 9, 1000), (300, 300, 7)):
+        a = float(np.sum(_rope(q, [m]) * _rope(k, [n])))
+        b = float(np.sum(_rope(q, [m + sh]) * _rope(k, [n + sh])))
+        assert abs(a - b) <= 1e-10, (m, n, sh, a, b)
+
+
+def pin_rope_cache_write():
+    """The store: token t's rotated key and (unrotated) value land in block
+    table[seq, p // 16], slot p % 16, of every KV head; nothing else changes; a negative
+    position or an entry outside the pool (when the pool size is given) writes nothing."""
+    rng = _rng(52)
+    T, Hq, Hkv, D, nb = 4, 4, 2, 8, 6
+    q = rng.standard_normal((T, Hq, D))
+    k = rng.standard_normal((T, Hkv, D))
+    v = rng.standard_normal((T, Hkv, D))
+    kc = rng.standard_normal((nb, Hkv, 16, D))
+    vc = rng.standard_normal((nb, Hkv, 16, D))
+    table = np.array([[3, 1, -1], [0, 5, 2], [4, 9, -1], [2, 2, 2]], dtype=np.int32)
+    pos = np.array([17, 40, 20, -1])
+    qr, kc2, vc2 = _rope_write(q, k, v, pos, kc, vc, table, base=10000.0, num_blocks=nb)
+    _close(qr, _rope(q, pos), 0.0, "rotated queries")
+    expect_k, expect_v = kc.copy(), vc.copy()
+    kr = _rope(k, pos)
+    for t, (blk, slot) in enumerate([(1, 1), (2, 8)]):   # tokens 0 and 1
+        expect_k[blk, :, slot, :] = kr[t]
+        expect_v[blk, :, slot, :] = v[t]
+    # token 2: table[2, 1] = 9 is outside the pool of 6; token 3: negative position
+    _close(kc2, expect_k, 0.0, "key cache")
+    _close(vc2, expect_v, 0.0, "value cache")
+    # an explicit sequence map: tokens 0 and 1 both belong to sequence 1
+    _, kc3, _ = _rope_write(q[:2], k[:2], v[:2], np.array([0, 33]), kc, vc, table,
+                            seq_ids=np.array([1, 1]))
+    _close(kc3[0, :, 0, :], _rope(k[:1], [0])[0], 0.0, "sequence map, token 0")
+    _close(kc3[2, :, 1, :], _rope(k[1:2], [33])[0], 0.0, "sequence map, token 1")
+
+
 ALL_PINS = [
     pin_rows_sum_to_one, pin_worked_row, pin_online_equals_two_pass, pin_split_merge,
     pin_stability, pin_masked_row, pin_identical_keys, pin_causal_row0, pin_degenerate,
     pin_brute_force, pin_shift_invariance, pin_v_affine, pin_gqa, pin_permutations,
     pin_decode_paged, pin_norm_residual_is_sum, pin_norm_unit_rms, pin_norm_scale_invariance,
-    pin_norm_constant_and_eps, pin_norm_brute_force,
+    pin_norm_constant_and_eps, pin_norm_brute_force, pin_rope_worked,
+    pin_rope_rotation_properties, pin_rope_cache_write,
 ]

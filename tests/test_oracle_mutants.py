@@ -8,6 +8,7 @@ import pytest
 
 import oracle.direct as OA
 import oracle.rmsnorm as ON
+import oracle.rotary as OR
 from tests import pins
 
 
@@ -192,4 +193,91 @@ def test_norm_mutant_is_caught(kind, monkeypatch):
 
 def test_unmutated_norm_copy_passes(monkeypatch):
     monkeypatch.setattr(ON, "add_rms_norm", _norm_mutant("none"))
+    assert _some_pin_fails() == []
+
+
+def _rope_mutant(kind):
+    def rope(x, positions, base=10000.0):
+        x = np.asarray(x, dtype=np.float64)
+        T, H, D = x.shape
+        half = D // 2
+        i = np.arange(half, dtype=np.float64)
+        if kind == "theta_half_exponent":
+            theta = np.power(float(base), -1.0 * i / D)
+        elif kind == "theta_positive":
+            theta = np.power(float(base), 2.0 * i / D)
+        else:
+            theta = np.power(float(base), -2.0 * i / D)
+        p = np.asarray(positions, dtype=np.float64) + (1 if kind == "position_plus_one" else 0)
+        ang = p[:, None] * theta[None, :]
+        c = np.cos(ang)[:, None, :]
+        s = np.sin(ang)[:, None, :]
+        if kind == "sin_sign":
+            s = -s
+        if kind == "interleaved":
+            x1, x2 = x[..., 0::2], x[..., 1::2]
+            y = np.empty_like(x)
+            y[..., 0::2] = x1 * c - x2 * s
+            y[..., 1::2] = x2 * c + x1 * s
+            return y
+        x1, x2 = x[..., :half], x[..., half:]
+        return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
+    return rope
+
+
+ROPE_MUTANTS = ["theta_half_exponent", "theta_positive", "position_plus_one", "sin_sign",
+                "interleaved"]
+
+
+@pytest.mark.parametrize("kind", ROPE_MUTANTS)
+def test_rope_mutant_is_caught(kind, monkeypatch):
+    monkeypatch.setattr(OR, "rope", _rope_mutant(kind))
+    failed = [f for f in _some_pin_fails() if f.startswith("pin_rope")]
+    assert failed, f"no pin catches mutant {kind}"
+
+
+def _rope_write_mutant(kind):
+    def write(q, k, v, positions, k_cache, v_cache, block_table, seq_ids=None, base=10000.0,
+              block_size=16, num_blocks=0):
+        q_rot = OR.rope(q, positions, base)
+        k_rot = OR.rope(k, positions, base) if kind != "key_unrotated" else np.asarray(k, float)
+        kc = np.array(k_cache, dtype=np.float64, copy=True)
+        vc = np.array(v_cache, dtype=np.float64, copy=True)
+        vv = OR.rope(v, positions, base) if kind == "value_rotated" else np.asarray(v, float)
+        for t in range(q_rot.shape[0]):
+            s = t if seq_ids is None else int(seq_ids[t])
+            p = int(positions[t])
+            if p < 0 and kind != "negative_written":
+                continue
+            if kind == "block_slot_swapped":
+                blk, slot = p % block_size, p // block_size
+            else:
+                blk, slot = p // block_size, p % block_size
+            if kind == "seq_map_ignored":
+                s = t
+            phys = int(block_table[s, blk])
+            if num_blocks > 0 and not (0 <= phys < num_blocks) and kind != "no_range_check":
+                continue
+            if kind == "no_range_check":
+                phys %= k_cache.shape[0]
+            kc[phys, :, slot, :] = k_rot[t]
+            vc[phys, :, slot, :] = vv[t]
+        return q_rot, kc, vc
+    return write
+
+
+ROPE_WRITE_MUTANTS = ["key_unrotated", "value_rotated", "negative_written",
+                      "block_slot_swapped", "seq_map_ignored", "no_range_check"]
+
+
+@pytest.mark.parametrize("kind", ROPE_WRITE_MUTANTS)
+def test_rope_write_mutant_is_caught(kind, monkeypatch):
+    monkeypatch.setattr(OR, "rope_cache_write", _rope_write_mutant(kind))
+    failed = [f for f in _some_pin_fails() if f.startswith("pin_rope")]
+    assert failed, f"no pin catches mutant {kind}"
+
+
+def test_unmutated_rope_copies_pass(monkeypatch):
+    monkeypatch.setattr(OR, "rope", _rope_mutant("none"))
+    monkeypatch.setattr(OR, "rope_cache_write", _rope_write_mutant("none"))
     assert _some_pin_fails() == []

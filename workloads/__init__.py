@@ -32,7 +32,7 @@ import numpy as np
 __all__ = [
     "FwdConfig", "DecodeConfig", "CONFIGS", "bf16_round", "bf16_bits", "bits_to_f32",
     "fwd_inputs", "decode_inputs", "DecodeInputs", "sample_rows", "NormConfig", "NORM_CONFIGS",
-    "norm_inputs", "norm_inputs_for",
+    "norm_inputs", "norm_inputs_for", "rope_inputs",
 ]
 
 
@@ -262,3 +262,16 @@ def norm_inputs(M, d, seed):
 
 def norm_inputs_for(cfg: NormConfig):
     return norm_inputs(cfg.M, cfg.d, cfg.seed)
+
+
+# ----------------------------------------------------------------------------------------
+# RoPE + cache-write inputs
+# ----------------------------------------------------------------------------------------
+def rope_inputs(T, Hq, Hkv, D, seed):
+    """Per-token projections q [T, Hq, D], k and v [T, Hkv, D] ~ N(0, 1), drawn in that order
+    and rounded to bfloat16 (returned as exact float32 arrays)."""
+    rng = np.random.default_rng(seed)
+    q = bf16_round(rng.standard_normal(size=(T, Hq, D), dtype=np.float32))
+    k = bf16_round(rng.standard_normal(size=(T, Hkv, D), dtype=np.float32))
+    v = bf16_round(rng.standard_normal(size=(T, Hkv, D), dtype=np.float32))
+    return q, k, v

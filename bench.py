@@ -192,6 +192,51 @@ def norm_timing(A, torch, dev, flush, flush_sink, stream, reps):
     return res
 
 
+def rope_timing(A, torch, dev, dq, dkc, dvc, dbt, dctx, flush, flush_sink, stream, reps):
+    """The fused RoPE + paged cache store: (1) the decode step's 64 new tokens (one per
+    sequence, at position ctx - 1, into the decode workload's own cache: the step that
+    precedes the decode), (2) a 2048-token prefill chunk of one sequence into a 128-block
+    pool. Each launch timed alone after the read flush. Algorithmic bytes: q, k, v read,
+    rotated q written, k and v stored (2 B per element each way) plus positions and table."""
+    B, Hq, D = dq.shape
+    Hkv = dkc.shape[1]
+    res = {}
+    rng = np.random.default_rng(7)
+    cases = []
+    pos = (dctx - 1).to(torch.int32)
+    mk = lambda shape: torch.from_numpy(
+        W.bf16_round(rng.standard_normal(shape, dtype=np.float32))).to(dev).to(torch.bfloat16)
+    cases.append(("decode_step_b64", mk((B, Hq, D)), mk((B, Hkv, D)), mk((B, Hkv, D)), pos,
+                  dkc, dvc, dbt, None))
+    T, nb = 2048, 128
+    cases.append(("prefill_chunk_2048", mk((T, Hq, D)), mk((T, Hkv, D)), mk((T, Hkv, D)),
+                  torch.arange(T, dtype=torch.int32, device=dev),
+                  torch.zeros((nb, Hkv, 16, D), dtype=torch.bfloat16, device=dev),
+                  torch.zeros((nb, Hkv, 16, D), dtype=torch.bfloat16, device=dev),
+                  torch.from_numpy(rng.permutation(nb).astype(np.int32)[None, :]).to(dev),
+                  torch.zeros(T, dtype=torch.int32, device=dev)))
+    for name, q, k, v, p, kc, vc, bt, seq in cases:
+        qo = torch.empty_like(q)
+        A.rope_cache_write(q, k, v, p, kc, vc, bt, seq_ids=seq, q_out=qo)
+        torch.cuda.synchronize()
+        ev = HipEvents(2 * reps)
+        for i in range(reps):
+            if flush is not None:
+                torch.sum(flush, dim=0, dtype=torch.int64, out=flush_sink[0])
+            ev.record(2 * i, stream)
+            A.rope_cache_write(q, k, v, p, kc, vc, bt, seq_ids=seq, q_out=qo)
+            ev.record(2 * i + 1, stream)
+        torch.cuda.synchronize()
+        us = float(np.median([ev.elapsed_ms(2 * i, 2 * i + 1) for i in range(reps)])) * 1e3
+        ev.close()
+        t = q.shape[0]
+        nbytes = 2.0 * t * D * (2 * Hq + 4 * Hkv) + 8.0 * t
+        gbs = nbytes / (us * 1e-6) / 1e9
+        res[name] = {"tokens": t, "us": round(us, 2), "bytes_per_launch": nbytes,
+                     "GB/s": round(gbs, 1), "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
+    return res
+
+
 def decode_graph_timing(A, torch, dq, dkc, dvc, dbt, dctx, scale, stream, reps):
     """The decode (stream + combine kernels) captured once into a hipGraph through
     attn_decode_paged_ex with a caller workspace, then replayed back to back: GPU time per
@@ -249,7 +294,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum host time for the oracle baseline (0 skips it)")
     ap.add_argument("--norm-reps", type=int, default=20,
-                    help="timed launches of the fused add_rms_norm per shape (0 = skip)")
+                    help="timed launches of the fused add_rms_norm and of the RoPE + cache "
+                         "write per shape (0 = skip both)")
     ap.add_argument("--graph-reps", type=int, default=50,
                     help="replays of the decode captured in a hipGraph (0 = skip that part)")
     ap.add_argument("--flush-mib", type=int, default=512,
@@ -337,6 +383,8 @@ def main():
                                 args.graph_reps) if args.graph_reps > 0 else None
     norm = norm_timing(A, torch, dev, flush, flush_sink, stream, args.norm_reps) \
         if args.norm_reps > 0 else None
+    rope = rope_timing(A, torch, dev, dq, dkc, dvc, dbt, dctx, flush, flush_sink, stream,
+                       args.norm_reps) if args.norm_reps > 0 else None
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     flops = prefill_flops(PREFILL)
     tflops = flops / (fwd_ms * 1e-3) / 1e12
@@ -384,6 +432,8 @@ def main():
         out["decode"]["hipgraph"] = graph
     if norm is not None:
         out["add_rms_norm"] = norm
+    if rope is not None:
+        out["rope_cache_write"] = rope
     if args.cpu_seconds > 0:
         out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(out), flush=True)

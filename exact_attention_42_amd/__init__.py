@@ -19,7 +19,7 @@ __all__ = [
     "attn_fwd", "attn_fwd_f32", "attn_decode_paged", "attn_decode_paged_ex",
     "attn_decode_workspace_bytes", "attn_decode_default_workers", "attn_status_string",
     "attn_last_error", "attn_release_workspace", "attn_abi_version", "attn_add_rms_norm",
-    "add_rms_norm", "EXPORTED_SYMBOLS",
+    "add_rms_norm", "attn_rope_cache_write", "rope_cache_write", "EXPORTED_SYMBOLS",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -40,6 +40,8 @@ _SIGNATURES = {
     "attn_release_workspace": (None, []),
     "attn_abi_version": (_I, []),
     "attn_add_rms_norm": (_I, [_P, _P, _P, _P, _P, _I, _I, _F, _P]),
+    "attn_rope_cache_write": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I,
+                                   _I, _I, _F, _P]),
 }
 EXPORTED_SYMBOLS = tuple(_SIGNATURES)
 
@@ -292,3 +294,47 @@ def add_rms_norm(x, residual, weight, eps=1e-6, out=None, residual_out=None, str
 def attn_add_rms_norm(*args, **kw):
     """Alias of :func:`add_rms_norm` under the C symbol's name."""
     return add_rms_norm(*args, **kw)
+
+
+def rope_cache_write(q, k, v, positions, k_cache, v_cache, block_table, seq_ids=None,
+                     base=10000.0, q_out=None, check_blocks=True, stream=None):
+    """Rotary embedding of q [T, Hq, D] and k [T, Hkv, D] at int32 ``positions`` [T], and the
+    store of the rotated keys and the values into the paged caches [num_blocks, Hkv, 16, D]
+    through ``block_table`` [num_seqs, stride] (token t belongs to sequence ``seq_ids[t]``,
+    or to sequence t when ``seq_ids`` is None). Returns the rotated queries (``q_out``, which
+    may be ``q``). ``check_blocks`` passes the pool size so out-of-range entries store
+    nothing."""
+    torch = _torch()
+    if q.dim() != 3 or k.dim() != 3 or k_cache.dim() != 4:
+        raise ValueError("q and k must be [T, H, D] and the caches [num_blocks, Hkv, 16, D]")
+    T, Hq, D = q.shape
+    nb, Hkv, bs, Dc = k_cache.shape
+    if tuple(k.shape) != (T, Hkv, D) or tuple(v.shape) != (T, Hkv, D) or Dc != D:
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} "
+                         f"v{tuple(v.shape)} cache{tuple(k_cache.shape)}")
+    dev = q.device
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _need(t, n, torch.bfloat16, dev)
+    _need(v_cache, "v_cache", torch.bfloat16, dev, tuple(k_cache.shape))
+    _need(positions, "positions", torch.int32, dev, (T,))
+    if block_table.dim() != 2:
+        raise ValueError("block_table must be [num_seqs, stride]")
+    _need(block_table, "block_table", torch.int32, dev)
+    if seq_ids is not None:
+        _need(seq_ids, "seq_ids", torch.int32, dev, (T,))
+    if q_out is None:
+        q_out = torch.empty_like(q)
+    _need(q_out, "q_out", torch.bfloat16, dev, (T, Hq, D))
+    with torch.cuda.device(dev):
+        _check(load_library().attn_rope_cache_write(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(q_out), _ptr(k_cache), _ptr(v_cache),
+            _ptr(block_table), _ptr(positions), _ptr(seq_ids), int(T),
+            int(block_table.shape[0]), int(Hq), int(Hkv), int(D), int(bs),
+            int(block_table.shape[1]), int(nb) if check_blocks else 0, float(base),
+            _stream_ptr(dev, stream)))
+    return q_out
+
+
+def attn_rope_cache_write(*args, **kw):
+    """Alias of :func:`rope_cache_write` under the C symbol's name."""
+    return rope_cache_write(*args, **kw)

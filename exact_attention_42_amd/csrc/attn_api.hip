@@ -215,9 +215,54 @@ int run_add_rms_norm(const void* x, const void* residual, const void* weight, vo
   return ok();
 }
 
+int run_rope_cache_write(const void* q, const void* k, const void* v, void* q_out,
+                         void* k_cache, void* v_cache, const int32_t* block_table,
+                         const int32_t* positions, const int32_t* seq_ids, int T, int num_seqs,
+                         int Hq, int Hkv, int D, int block_size, int table_stride,
+                         int num_blocks, float base, void* stream) {
+  if (T < 0 || num_seqs < 0)
+    return fail(ATTN_ERR_SHAPE, "T and num_seqs must be >= 0 (T=%d num_seqs=%d)", T, num_seqs);
+  if (Hq < 1 || Hkv < 1 || table_stride < 1)
+    return fail(ATTN_ERR_SHAPE, "need Hq >= 1, Hkv >= 1 and table_stride >= 1 (Hq=%d Hkv=%d "
+                "table_stride=%d)", Hq, Hkv, table_stride);
+  if (!seq_ids && T > num_seqs)
+    return fail(ATTN_ERR_SHAPE, "without seq_ids token t is sequence t, so T=%d must be <= "
+                "num_seqs=%d", T, num_seqs);
+  if (D != 64 && D != 128)
+    return fail(ATTN_ERR_UNSUPPORTED, "head dimension D=%d not supported (64 or 128)", D);
+  if (block_size != 16)
+    return fail(ATTN_ERR_UNSUPPORTED, "block_size=%d not supported (16)", block_size);
+  if (!std::isfinite(base) || !(base > 0.f))
+    return fail(ATTN_ERR_SCALE, "rope base must be finite and > 0 (got %g)", (double)base);
+  if (T == 0) return ok();
+  if (!q || !k || !v || !q_out || !k_cache || !v_cache || !block_table || !positions)
+    return fail(ATTN_ERR_NULL, "q, k, v, q_out, k_cache, v_cache, block_table and positions "
+                "must not be NULL");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(q_out, 16) ||
+      !aligned(k_cache, 16) || !aligned(v_cache, 16))
+    return fail(ATTN_ERR_ALIGN, "q, k, v, q_out, k_cache and v_cache must be 16-byte aligned");
+  if (!aligned(block_table, 4) || !aligned(positions, 4) || (seq_ids && !aligned(seq_ids, 4)))
+    return fail(ATTN_ERR_ALIGN, "block_table, positions and seq_ids must be 4-byte aligned");
+  attn::RopeProblem p{q, k, v, q_out, k_cache, v_cache, block_table, positions, seq_ids,
+                      T, num_seqs, Hq, Hkv, D, table_stride, num_blocks, base};
+  hipError_t e = attn::launch_rope_cache_write(p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "attn_rope_cache_write launch");
+  return ok();
+}
+
 }  // namespace
 
 extern "C" {
+
+int attn_rope_cache_write(const void* q, const void* k, const void* v, void* q_out,
+                          void* k_cache, void* v_cache, const int32_t* block_table,
+                          const int32_t* positions, const int32_t* seq_ids, int T,
+                          int num_seqs, int Hq, int Hkv, int D, int block_size,
+                          int table_stride, int num_blocks, float base, void* stream) {
+  return run_rope_cache_write(q, k, v, q_out, k_cache, v_cache, block_table, positions,
+                              seq_ids, T, num_seqs, Hq, Hkv, D, block_size, table_stride,
+                              num_blocks, base, stream);
+}
 
 int attn_add_rms_norm(const void* x, const void* residual, const void* weight, void* out,
                       void* residual_out, int M, int d, float eps, void* stream) {
@@ -291,6 +336,6 @@ void attn_release_workspace(void) {
   if (have_cur) (void)hipSetDevice(cur);
 }
 
-int attn_abi_version(void) { return 4; }
+int attn_abi_version(void) { return 5; }
 
 }  // extern "C"

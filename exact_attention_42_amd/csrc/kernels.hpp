@@ -58,4 +58,22 @@ struct NormProblem {
 int add_rms_norm_threads(int d);
 hipError_t launch_add_rms_norm(const NormProblem& p, hipStream_t stream);
 
+struct RopeProblem {
+  const void* q;            // [T, Hq, D] bf16
+  const void* k;            // [T, Hkv, D] bf16
+  const void* v;            // [T, Hkv, D] bf16
+  void* q_out;              // [T, Hq, D] bf16 (may be q)
+  void* k_cache;            // [num_blocks, Hkv, 16, D] bf16
+  void* v_cache;
+  const int32_t* block_table;  // [num_seqs, table_stride]
+  const int32_t* positions;    // [T]
+  const int32_t* seq_ids;      // [T] or null (token t is sequence t)
+  int T, num_seqs, Hq, Hkv, D;
+  int table_stride;
+  int num_blocks;           // <= 0: unchecked
+  float base;
+};
+
+hipError_t launch_rope_cache_write(const RopeProblem& p, hipStream_t stream);
+
 }  // namespace attn

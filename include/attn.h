@@ -137,6 +137,36 @@ int attn_decode_default_workers(void);
 int attn_add_rms_norm(const void* x, const void* residual, const void* weight, void* out,
                       void* residual_out, int M, int d, float eps, void* stream);
 
+/* Fused rotary position embedding + paged KV-cache store, the step before decode attention
+ * ("Kernel and Operator Fusion -- Inference Optimization", §2 item 6, RoPE then KV store).
+ * For every token t at position p = positions[t] of sequence s = seq_ids[t] (s = t when
+ * seq_ids is NULL), with theta_i = base^(-2i/D) for i < D/2:
+ *   every query head and key head: element i and element i + D/2 turn by p * theta_i
+ *     (y_i = x_i cos - x_{i+D/2} sin, y_{i+D/2} = x_{i+D/2} cos + x_i sin);
+ *   q_out[t] = rotated q[t];
+ *   k_cache[b, h, p % 16, :] = rotated k[t, h], v_cache[b, h, p % 16, :] = v[t, h], where
+ *     b = block_table[s * table_stride + p / 16] -- the layout attn_decode_paged reads.
+ *   q, q_out:          [T, Hq, D] bf16 (q_out may be q: in place)
+ *   k, v:              [T, Hkv, D] bf16
+ *   k_cache, v_cache:  [num_blocks, Hkv, block_size, D] bf16, updated in place
+ *   block_table:       [num_seqs, table_stride] int32; positions [T] int32;
+ *   seq_ids:           [T] int32 or NULL (then T <= num_seqs)
+ *   num_blocks:        pool size; > 0 makes the kernel skip the store of a token whose table
+ *                      entry is outside [0, num_blocks); <= 0 = unchecked
+ * A token stores nothing when p < 0, p / 16 >= table_stride, s is outside [0, num_seqs) or
+ * (checked) its entry is outside the pool; its query is rotated regardless. The angle and its
+ * sine and cosine are evaluated in fp64, the rotation in fp32, each output rounded to bf16
+ * (nearest even) once; values are copied exactly. Two tokens that map to the same slot race.
+ * Requirements: D in {64, 128}, block_size 16 (ATTN_ERR_UNSUPPORTED); T, num_seqs >= 0,
+ * Hq, Hkv, table_stride >= 1 (ATTN_ERR_SHAPE); base finite and > 0 (ATTN_ERR_SCALE);
+ * pointers non-NULL (seq_ids may be NULL) and aligned: 16 bytes for the bf16 tensors, 4 for
+ * the int32 arrays (ATTN_ERR_NULL, ATTN_ERR_ALIGN). T == 0 is a no-op. One kernel on stream. */
+int attn_rope_cache_write(const void* q, const void* k, const void* v, void* q_out,
+                          void* k_cache, void* v_cache, const int32_t* block_table,
+                          const int32_t* positions, const int32_t* seq_ids, int T,
+                          int num_seqs, int Hq, int Hkv, int D, int block_size,
+                          int table_stride, int num_blocks, float base, void* stream);
+
 /* Static text for a status code. */
 const char* attn_status_string(int status);
 
@@ -146,7 +176,7 @@ const char* attn_last_error(void);
 /* Frees the library-owned decode workspaces (synchronises the devices that hold them). */
 void attn_release_workspace(void);
 
-/* ABI version of this header: 4. */
+/* ABI version of this header: 5. */
 int attn_abi_version(void);
 
 #ifdef __cplusplus

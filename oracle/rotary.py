@@ -41,8 +41,9 @@ def rope_cache_write(q, k, v, positions, k_cache, v_cache, block_table, seq_ids=
                      base=10000.0, block_size=16, num_blocks=0):
     """Rotates q [T, Hq, D] and k [T, Hkv, D] by their token's position, then stores the
     rotated k and the unrotated v of token t into the caches (copies, float64) at the slot
-    its sequence's block table gives. Tokens whose position is negative, or whose table entry
-    falls outside [0, num_blocks) when num_blocks > 0, leave the caches untouched.
+    its sequence's block table gives. Tokens whose position is negative or lies past the end
+    of the table row, or whose table entry falls outside [0, num_blocks) when num_blocks > 0,
+    leave the caches untouched.
     Returns (q_rot, k_cache_out, v_cache_out)."""
     q_rot = rope(q, positions, base)
     k_rot = rope(k, positions, base)
@@ -52,7 +53,7 @@ def rope_cache_write(q, k, v, positions, k_cache, v_cache, block_table, seq_ids=
     for t in range(q_rot.shape[0]):
         s = t if seq_ids is None else int(seq_ids[t])
         p = int(positions[t])
-        if p < 0:
+        if p < 0 or p // block_size >= block_table.shape[1]:
             continue
         phys = int(block_table[s, p // block_size])
         if num_blocks > 0 and not (0 <= phys < num_blocks):

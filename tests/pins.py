@@ -546,16 +546,17 @@ def pin_rope_rotation_properties():
 def pin_rope_cache_write():
     """The store: token t's rotated key and (unrotated) value land in block
     table[seq, p // 16], slot p % 16, of every KV head; nothing else changes; a negative
-    position or an entry outside the pool (when the pool size is given) writes nothing."""
+    position, a position past the table row, or an entry outside the pool (when the pool size
+    is given) writes nothing."""
     rng = _rng(52)
-    T, Hq, Hkv, D, nb = 4, 4, 2, 8, 6
+    T, Hq, Hkv, D, nb = 5, 4, 2, 8, 6
     q = rng.standard_normal((T, Hq, D))
     k = rng.standard_normal((T, Hkv, D))
     v = rng.standard_normal((T, Hkv, D))
     kc = rng.standard_normal((nb, Hkv, 16, D))
     vc = rng.standard_normal((nb, Hkv, 16, D))
-    table = np.array([[3, 1, -1], [0, 5, 2], [4, 9, -1], [2, 2, 2]], dtype=np.int32)
-    pos = np.array([17, 40, 20, -1])
+    table = np.array([[3, 1, -1], [0, 5, 2], [4, 9, -1], [2, 2, 2], [1, 1, 1]], dtype=np.int32)
+    pos = np.array([17, 40, 20, -1, 48])
     qr, kc2, vc2 = _rope_write(q, k, v, pos, kc, vc, table, base=10000.0, num_blocks=nb)
     _close(qr, _rope(q, pos), 0.0, "rotated queries")
     expect_k, expect_v = kc.copy(), vc.copy()
@@ -563,7 +564,8 @@ def pin_rope_cache_write():
     for t, (blk, slot) in enumerate([(1, 1), (2, 8)]):   # tokens 0 and 1
         expect_k[blk, :, slot, :] = kr[t]
         expect_v[blk, :, slot, :] = v[t]
-    # token 2: table[2, 1] = 9 is outside the pool of 6; token 3: negative position
+    # token 2: table[2, 1] = 9 is outside the pool of 6; token 3: negative position;
+    # token 4: position 48 is block 3, past its table row of 3 entries
     _close(kc2, expect_k, 0.0, "key cache")
     _close(vc2, expect_v, 0.0, "value cache")
     # an explicit sequence map: tokens 0 and 1 both belong to sequence 1

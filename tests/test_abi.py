@@ -42,7 +42,7 @@ def test_status_strings_and_version():
     for code in range(9):
         assert A.attn_status_string(code) not in ("", "unknown status")
     assert A.attn_status_string(99) == "unknown status"
-    assert A.attn_abi_version() == 4
+    assert A.attn_abi_version() == 5
 
 
 def fwd(*, q=P, k=P, v=P, o=P, lse=0, B=1, Hq=32, Hkv=8, Sq=128, Sk=128, D=128, causal=1,
@@ -187,3 +187,29 @@ def test_norm_binding_checks_shapes():
         A.add_rms_norm(x, x, torch.zeros(16, dtype=torch.bfloat16))
     with pytest.raises(ValueError, match="must match"):
         A.add_rms_norm(x, torch.zeros(2, 8, dtype=torch.bfloat16), x[0])
+
+
+def rope(*, q=P, k=P, v=P, qo=P, kc=P, vc=P, table=P, pos=P, seq=0, T=4, nseq=4, Hq=32, Hkv=8,
+         D=128, bs=16, stride=8, nblocks=0, base=10000.0):
+    return A.load_library().attn_rope_cache_write(q, k, v, qo, kc, vc, table, pos, seq, T, nseq,
+                                                   Hq, Hkv, D, bs, stride, nblocks, base, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), NULL), (dict(k=0), NULL), (dict(v=0), NULL), (dict(qo=0), NULL),
+    (dict(kc=0), NULL), (dict(vc=0), NULL), (dict(table=0), NULL), (dict(pos=0), NULL),
+    (dict(T=-1), SHAPE), (dict(nseq=-1), SHAPE), (dict(Hq=0), SHAPE), (dict(Hkv=0), SHAPE),
+    (dict(stride=0), SHAPE), (dict(T=5, nseq=4), SHAPE), (dict(D=96), UNSUP),
+    (dict(bs=32), UNSUP), (dict(base=NAN), SCALE), (dict(base=0.0), SCALE),
+    (dict(base=-2.0), SCALE), (dict(q=P + 8), ALIGN), (dict(vc=P + 2), ALIGN),
+    (dict(pos=P + 2), ALIGN), (dict(seq=P + 1), ALIGN),
+])
+def test_rope_rejects(kw, code):
+    assert rope(**kw) == code
+    assert A.attn_last_error() != ""
+
+
+def test_rope_empty_and_sequence_map():
+    assert rope(T=0, q=0, k=0, v=0, qo=0, kc=0, vc=0, table=0, pos=0) == OK
+    # with a sequence map, more tokens than table rows is fine (the check is per token)
+    assert rope(T=9, nseq=4, seq=P, q=0) == NULL

@@ -249,13 +249,15 @@ def _rope_write_mutant(kind):
             p = int(positions[t])
             if p < 0 and kind != "negative_written":
                 continue
+            if p // block_size >= block_table.shape[1] and kind != "past_row_written":
+                continue
             if kind == "block_slot_swapped":
                 blk, slot = p % block_size, p // block_size
             else:
                 blk, slot = p // block_size, p % block_size
             if kind == "seq_map_ignored":
                 s = t
-            phys = int(block_table[s, blk])
+            phys = int(block_table[s, min(blk, block_table.shape[1] - 1)])
             if num_blocks > 0 and not (0 <= phys < num_blocks) and kind != "no_range_check":
                 continue
             if kind == "no_range_check":
@@ -267,7 +269,8 @@ def _rope_write_mutant(kind):
 
 
 ROPE_WRITE_MUTANTS = ["key_unrotated", "value_rotated", "negative_written",
-                      "block_slot_swapped", "seq_map_ignored", "no_range_check"]
+                      "block_slot_swapped", "seq_map_ignored", "no_range_check",
+                      "past_row_written"]
 
 
 @pytest.mark.parametrize("kind", ROPE_WRITE_MUTANTS)

@@ -237,6 +237,35 @@ def rope_timing(A, torch, dev, dq, dkc, dvc, dbt, dctx, flush, flush_sink, strea
     return res
 
 
+def chunked_prefill_timing(A, torch, dev, stream, reps):
+    """The chunked-prefill step (§8(f) N3 workload): the last 512 tokens of a 4096-token
+    prompt against the whole prefix, bottom-right causal. Its 128 query tiles cannot fill the
+    device, so the forward splits each tile's keys; timed back to back (compute-bound)."""
+    cfg = W.CONFIGS["chunked_prefill_512_of_4096"]
+    q, k, v = W.fwd_inputs_for(cfg)
+    bf = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev).to(torch.bfloat16)
+    qg, kg, vg = bf(q), bf(k), bf(v)
+    o = torch.empty_like(qg)
+    lse = torch.empty(qg.shape[:3], dtype=torch.float32, device=dev)
+    call = lambda: A.attn_fwd(qg, kg, vg, causal=True, scale=float(cfg.scale), out=o, lse=lse)
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    ev = HipEvents(2)
+    ev.record(0, stream)
+    for _ in range(reps):
+        call()
+    ev.record(1, stream)
+    torch.cuda.synchronize()
+    us = ev.elapsed_ms(0, 1) * 1e3 / reps
+    ev.close()
+    tf = prefill_flops(cfg) / (us * 1e-6) / 1e12
+    return {"workload": "B=1 Hq=32 Hkv=8 Sq=512 Sk=4096 D=128 causal (bottom-right) bf16",
+            "us": round(us, 2), "flops_per_launch": prefill_flops(cfg),
+            "tflops": round(tf, 2), "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+            "key_splits": A.attn_fwd_workspace_bytes(1, 32, 8, 512, 4096, 128, True) > 0}
+
+
 def decode_graph_timing(A, torch, dq, dkc, dvc, dbt, dctx, scale, stream, reps):
     """The decode (stream + combine kernels) captured once into a hipGraph through
     attn_decode_paged_ex with a caller workspace, then replayed back to back: GPU time per
@@ -385,6 +414,7 @@ def main():
         if args.norm_reps > 0 else None
     rope = rope_timing(A, torch, dev, dq, dkc, dvc, dbt, dctx, flush, flush_sink, stream,
                        args.norm_reps) if args.norm_reps > 0 else None
+    chunk = chunked_prefill_timing(A, torch, dev, stream, 20) if args.norm_reps > 0 else None
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     flops = prefill_flops(PREFILL)
     tflops = flops / (fwd_ms * 1e-3) / 1e12
@@ -434,6 +464,8 @@ def main():
         out["add_rms_norm"] = norm
     if rope is not None:
         out["rope_cache_write"] = rope
+    if chunk is not None:
+        out["chunked_prefill"] = chunk
     if args.cpu_seconds > 0:
         out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(out), flush=True)

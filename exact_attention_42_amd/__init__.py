@@ -16,7 +16,8 @@ import os
 
 __all__ = [
     "AttnError", "library_path", "load_library",
-    "attn_fwd", "attn_fwd_f32", "attn_decode_paged", "attn_decode_paged_ex",
+    "attn_fwd", "attn_fwd_f32", "attn_fwd_ex", "attn_fwd_workspace_bytes", "attn_decode_paged",
+    "attn_decode_paged_ex",
     "attn_decode_workspace_bytes", "attn_decode_default_workers", "attn_status_string",
     "attn_last_error", "attn_release_workspace", "attn_abi_version", "attn_add_rms_norm",
     "add_rms_norm", "attn_rope_cache_write", "rope_cache_write", "EXPORTED_SYMBOLS",
@@ -30,6 +31,8 @@ _P, _I, _F, _Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
 _SIGNATURES = {
     "attn_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P]),
     "attn_fwd_f32": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P]),
+    "attn_fwd_ex": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P, _Z, _P]),
+    "attn_fwd_workspace_bytes": (_Z, [_I, _I, _I, _I, _I, _I, _I]),
     "attn_decode_paged": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P]),
     "attn_decode_paged_ex": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I,
                                   _I, _P, _Z, _P]),
@@ -155,7 +158,7 @@ def _need(t, name, dtype, device, shape=None):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
 
 
-def _fwd(fn_name, dtype, q, k, v, causal, scale, out, lse, want_lse, stream):
+def _fwd(fn_name, dtype, q, k, v, causal, scale, out, lse, want_lse, stream, workspace=None):
     torch = _torch()
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("q, k, v must be [B, H, S, D]")
@@ -176,18 +179,36 @@ def _fwd(fn_name, dtype, q, k, v, causal, scale, out, lse, want_lse, stream):
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     fn = getattr(load_library(), fn_name)
+    args = [_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Sq, Sk, D,
+            1 if causal else 0, float(scale)]
+    if fn_name == "attn_fwd_ex":
+        if workspace is not None:
+            _need(workspace, "workspace", torch.uint8, dev)
+        args += [_ptr(workspace), int(workspace.numel()) if workspace is not None else 0]
     with torch.cuda.device(dev):
-        _check(fn(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Sq, Sk, D,
-                  1 if causal else 0, float(scale), _stream_ptr(dev, stream)))
+        _check(fn(*args, _stream_ptr(dev, stream)))
     return out, lse
 
 
-def attn_fwd(q, k, v, causal=False, scale=None, out=None, lse=None, want_lse=True, stream=None):
+def attn_fwd(q, k, v, causal=False, scale=None, out=None, lse=None, want_lse=True, stream=None,
+             workspace=None):
     """bf16 forward. q [B,Hq,Sq,D], k/v [B,Hkv,Sk,D] (bfloat16, contiguous, same GPU).
 
     Returns (out [B,Hq,Sq,D] bf16, lse [B,Hq,Sq] fp32 or None). ``scale`` defaults to
-    1/sqrt(D). The work is enqueued on ``stream`` (default: torch's current stream)."""
-    return _fwd("attn_fwd", _torch().bfloat16, q, k, v, causal, scale, out, lse, want_lse, stream)
+    1/sqrt(D). The work is enqueued on ``stream`` (default: torch's current stream).
+    ``workspace`` is an optional uint8 device tensor of at least attn_fwd_workspace_bytes(...)
+    bytes for the key-range splits of few-tile problems (None: the library's own)."""
+    return _fwd("attn_fwd_ex", _torch().bfloat16, q, k, v, causal, scale, out, lse, want_lse,
+                stream, workspace)
+
+
+def attn_fwd_ex(*args, **kw):
+    """Alias of :func:`attn_fwd` (which always goes through the C entry point attn_fwd_ex)."""
+    return attn_fwd(*args, **kw)
+
+
+def attn_fwd_workspace_bytes(B, Hq, Hkv, Sq, Sk, D, causal) -> int:
+    return load_library().attn_fwd_workspace_bytes(B, Hq, Hkv, Sq, Sk, D, 1 if causal else 0)
 
 
 def attn_fwd_f32(q, k, v, causal=False, scale=None, out=None, lse=None, want_lse=True,

@@ -74,29 +74,26 @@ int check_fwd(const void* q, const void* k, const void* v, void* o, const float*
   return ATTN_OK;
 }
 
-int run_fwd(bool f32, const void* q, const void* k, const void* v, void* o, float* lse, int B,
-            int Hq, int Hkv, int Sq, int Sk, int D, int causal, float scale, void* stream) {
-  bool empty;
-  if (int rc = check_fwd(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, &empty)) return rc;
-  // the bf16 kernel addresses one head's K (and V) through a buffer resource with 32-bit
-  // signed offsets
-  if (!f32 && (long long)Sk * D * 2 > 0x7fffffffLL)
-    return fail(ATTN_ERR_SHAPE, "Sk=%d too long for D=%d: Sk*D*2 must stay below 2^31", Sk, D);
-  if (empty) return ok();
-  attn::FwdProblem p{q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, causal ? 1 : 0, scale};
-  hipError_t e = f32 ? attn::launch_fwd_f32(p, static_cast<hipStream_t>(stream))
-                     : attn::launch_fwd_bf16(p, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, f32 ? "attn_fwd_f32 launch" : "attn_fwd launch");
-  return ok();
-}
-
-// ---- decode workspace owned by the library: one buffer per (device, stream) ----
+// ---- workspace owned by the library: one buffer per (device, stream), shared by the decode's
+// partial results and the split forward's (calls on one stream run in order) ----
 struct Workspace {
   void* ptr = nullptr;
   size_t bytes = 0;
 };
 std::mutex g_ws_mutex;
 std::map<std::pair<int, void*>, Workspace> g_ws;
+
+// Compute units of the current device (256 when it cannot be queried).
+int device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0) {
+    (void)hipGetLastError();
+    cus = 256;
+  }
+  return cus;
+}
 
 // Worker waves when the caller passes 0: three per CU of the current device, which measured
 // fastest (more concurrent block streams only add memory-side contention; fewer leave HBM
@@ -108,13 +105,7 @@ int default_workers() {
     return (x >= 1 && x <= kMaxWorkers) ? x : 0;
   }();
   if (env) return env;
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      cus <= 0) {
-    (void)hipGetLastError();
-    cus = 256;
-  }
+  const int cus = device_cus();
   const int w = 3 * cus;
   return w > kMaxWorkers ? kMaxWorkers : w;
 }
@@ -126,6 +117,14 @@ int get_workspace(void* stream, size_t need, void** out) {
   std::lock_guard<std::mutex> lock(g_ws_mutex);
   Workspace& w = g_ws[{dev, stream}];
   if (w.bytes < need) {
+    // growing allocates (and frees, which synchronises): not while a graph is being captured
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(static_cast<hipStream_t>(stream), &cap) == hipSuccess &&
+        cap != hipStreamCaptureStatusNone)
+      return fail(ATTN_ERR_WORKSPACE, "this call needs %zu bytes of library workspace on a "
+                  "stream that is being captured; pass a caller workspace (the _ex entry "
+                  "points) or make the same call on this stream before capturing", need);
+    (void)hipGetLastError();
     if (w.ptr) {
       e = hipFree(w.ptr);   // synchronises: in-flight kernels may still read the old buffer
       w.ptr = nullptr;
@@ -137,12 +136,45 @@ int get_workspace(void* stream, size_t need, void** out) {
     if (e != hipSuccess) {
       w.ptr = nullptr;
       (void)hipGetLastError();
-      return fail(ATTN_ERR_NOMEM, "decode workspace of %zu bytes: %s", sz, hipGetErrorString(e));
+      return fail(ATTN_ERR_NOMEM, "workspace of %zu bytes: %s", sz, hipGetErrorString(e));
     }
     w.bytes = sz;
   }
   *out = w.ptr;
   return ATTN_OK;
+}
+
+int run_fwd(bool f32, const void* q, const void* k, const void* v, void* o, float* lse, int B,
+            int Hq, int Hkv, int Sq, int Sk, int D, int causal, float scale, void* workspace,
+            size_t workspace_bytes, void* stream) {
+  bool empty;
+  if (int rc = check_fwd(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, &empty)) return rc;
+  // the bf16 kernel addresses one head's K (and V) through a buffer resource with 32-bit
+  // signed offsets
+  if (!f32 && (long long)Sk * D * 2 > 0x7fffffffLL)
+    return fail(ATTN_ERR_SHAPE, "Sk=%d too long for D=%d: Sk*D*2 must stay below 2^31", Sk, D);
+  if (empty) return ok();
+  attn::FwdProblem p{q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, causal ? 1 : 0, scale, 1, nullptr};
+  if (!f32) {
+    p.nsplit = attn::fwd_bf16_splits(p, device_cus());
+    if (p.nsplit > 1) {
+      const size_t need = attn::fwd_bf16_workspace_bytes(p, p.nsplit);
+      if (workspace) {
+        if (workspace_bytes < need)
+          return fail(ATTN_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed",
+                      workspace_bytes, need);
+        if (!aligned(workspace, 16))
+          return fail(ATTN_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+        p.workspace = workspace;
+      } else if (int rc = get_workspace(stream, need, &p.workspace)) {
+        return rc;
+      }
+    }
+  }
+  hipError_t e = f32 ? attn::launch_fwd_f32(p, static_cast<hipStream_t>(stream))
+                     : attn::launch_fwd_bf16(p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, f32 ? "attn_fwd_f32 launch" : "attn_fwd launch");
+  return ok();
 }
 
 int run_decode(const void* q, const void* k_cache, const void* v_cache,
@@ -271,12 +303,30 @@ int attn_add_rms_norm(const void* x, const void* residual, const void* weight, v
 
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
              int Hkv, int Sq, int Sk, int D, int causal, float scale, void* stream) {
-  return run_fwd(false, q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, causal, scale, stream);
+  return run_fwd(false, q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, causal, scale, nullptr, 0,
+                 stream);
 }
 
 int attn_fwd_f32(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                  int Hq, int Hkv, int Sq, int Sk, int D, int causal, float scale, void* stream) {
-  return run_fwd(true, q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, causal, scale, stream);
+  return run_fwd(true, q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, causal, scale, nullptr, 0,
+                 stream);
+}
+
+int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+                int Hkv, int Sq, int Sk, int D, int causal, float scale, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  return run_fwd(false, q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, causal, scale, workspace,
+                 workspace_bytes, stream);
+}
+
+size_t attn_fwd_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk, int D, int causal) {
+  if (B < 0 || Sq < 0 || Sk < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || (D != 64 && D != 128) ||
+      (long long)B * Hq > 0x7fffffffLL || Sq > (1 << 30) || Sk > (1 << 30))
+    return 0;
+  attn::FwdProblem p{nullptr, nullptr, nullptr, nullptr, nullptr, B, Hq, Hkv, Sq, Sk, D,
+                     causal ? 1 : 0, 1.0f, 1, nullptr};
+  return attn::fwd_bf16_workspace_bytes(p, attn::fwd_bf16_splits(p, device_cus()));
 }
 
 int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
@@ -336,6 +386,6 @@ void attn_release_workspace(void) {
   if (have_cur) (void)hipSetDevice(cur);
 }
 
-int attn_abi_version(void) { return 5; }
+int attn_abi_version(void) { return 6; }
 
 }  // extern "C"

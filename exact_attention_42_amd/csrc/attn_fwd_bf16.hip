@@ -59,6 +59,9 @@ constexpr int kBN = 64;            // keys per K/V tile
 constexpr float kLazy = 8.0f;      // log2 of the largest probability allowed before rescaling
 // Pair kernel is used for causal launches with at most this many tiles per head.
 constexpr int kPairMaxTiles = 64;
+// Most key-range splits per query tile (the split path serves few-tile problems, such as a
+// prefill chunk against a long prefix, whose query tiles alone would leave CUs idle).
+constexpr int kMaxFwdSplits = 8;
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
@@ -94,6 +97,9 @@ struct FwdArgs {
   int npairs;      // pair kernel: work items per (batch, query head)
   int nitems;      // pair kernel: B * Hq * npairs
   float c;         // scale * log2(e), > 0
+  int nsplit;      // split kernel: key-range splits per query tile
+  float* part_o;   // split kernel: [nsplit][B*Hq*Sq][D] unnormalised partial outputs
+  float* part_ml;  // split kernel: [nsplit][B*Hq*Sq][2] (reference max, sum)
 };
 
 // Buffer resource word 3 for raw (untyped) loads on gfx9-family parts.
@@ -324,7 +330,10 @@ __device__ __forceinline__ int xcd_item(int id, int n) {
   return x < r ? x * (q + 1) + s : r * (q + 1) + (x - r) * q + s;
 }
 
-template <int D, bool CAUSAL>
+// SPLIT: the workgroup covers one of a.nsplit contiguous ranges of the query tile's key tiles
+// and writes its unnormalised partial result (O, reference max, sum) to the workspace; the
+// split combine kernel merges the ranges. Otherwise it covers all the tile's keys.
+template <int D, bool CAUSAL, bool SPLIT>
 __device__ __forceinline__ void fwd_tile_body(const FwdArgs& a) {
   using G = Geo<D, 4>;
   // two stages, each a K tile and a V tile; separate objects so the compiler can tell the
@@ -343,8 +352,10 @@ __device__ __forceinline__ void fwd_tile_body(const FwdArgs& a) {
   // ---- work item: heaviest tiles first, all heads of one rank together ----
   const int BH = a.B * a.Hq;
   const int id = blockIdx.x;
-  const int rank = id / BH;
-  const int bh = id - rank * BH;
+  const int unit = id / BH;                // rank * nsplit + split
+  const int bh = id - unit * BH;
+  const int rank = SPLIT ? unit / a.nsplit : unit;
+  const int split = SPLIT ? unit - rank * a.nsplit : 0;
   const int tile = CAUSAL ? (a.ntq - 1 - rank) : rank;
   const int b = bh / a.Hq;
   const int hq = bh - b * a.Hq;
@@ -360,7 +371,10 @@ __device__ __forceinline__ void fwd_tile_body(const FwdArgs& a) {
   // ---- keys this workgroup visits ----
   int kv_end = a.Sk;
   if (CAUSAL) kv_end = min(a.Sk, max(0, q0 + kBM + off));
-  const int ntiles = (kv_end + kBN - 1) / kBN;
+  const int nall = (kv_end + kBN - 1) / kBN;
+  // this workgroup's key tiles [t0, t0 + ntiles)
+  const int t0 = SPLIT ? split * nall / a.nsplit : 0;
+  const int ntiles = SPLIT ? (split + 1) * nall / a.nsplit - t0 : nall;
 
   WaveState<D> w;
   {
@@ -401,21 +415,43 @@ __device__ __forceinline__ void fwd_tile_body(const FwdArgs& a) {
 
   TileDma<D, 4> dma;
   dma.init(wave, lane, kbase, vbase, a.Sk);
-  if (ntiles > 0) dma.issue(sk0, sv0, 0, a.Sk);
+  if (ntiles > 0) dma.issue(sk0, sv0, t0 * kBN, a.Sk);
   wait_dma_and_barrier();
 
   for (int j = 0; j < ntiles; j += 2) {
+    const int kt = (t0 + j) * kBN;
     // stage 0 holds tile j; prefetch tile j+1 into stage 1
-    if (j + 1 < ntiles) dma.issue(sk1, sv1, (j + 1) * kBN, a.Sk);
-    compute_tile<D, CAUSAL>(w, sk0, sv0, j * kBN, a.Sk, qw, wave_last_key, my_q, off, h, c,
-                            false);
+    if (j + 1 < ntiles) dma.issue(sk1, sv1, kt + kBN, a.Sk);
+    compute_tile<D, CAUSAL>(w, sk0, sv0, kt, a.Sk, qw, wave_last_key, my_q, off, h, c, false);
     wait_dma_and_barrier();
     if (j + 1 >= ntiles) break;
     // stage 1 holds tile j+1; prefetch tile j+2 into stage 0
-    if (j + 2 < ntiles) dma.issue(sk0, sv0, (j + 2) * kBN, a.Sk);
-    compute_tile<D, CAUSAL>(w, sk1, sv1, (j + 1) * kBN, a.Sk, qw, wave_last_key, my_q, off, h,
-                            c, false);
+    if (j + 2 < ntiles) dma.issue(sk0, sv0, kt + 2 * kBN, a.Sk);
+    compute_tile<D, CAUSAL>(w, sk1, sv1, kt + kBN, a.Sk, qw, wave_last_key, my_q, off, h, c,
+                            false);
     wait_dma_and_barrier();
+  }
+
+  if (SPLIT) {
+    // ---- partial result: unnormalised O, reference max (base 2, scaled) and sum ----
+    const float l_tot = xor32_sum(w.l_run);
+    if (my_q < a.Sq) {
+      const size_t prow = (size_t)split * BH * a.Sq + (size_t)bh * a.Sq + my_q;
+      float* po = a.part_o + prow * D;
+#pragma unroll
+      for (int db = 0; db < G::DB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d = 32 * db + 8 * g + 4 * h;
+          *reinterpret_cast<f32x4*>(po + d) =
+              f32x4{w.o[db][4 * g + 0], w.o[db][4 * g + 1], w.o[db][4 * g + 2],
+                    w.o[db][4 * g + 3]};
+        }
+      if (h == 0)
+        *reinterpret_cast<f32x2*>(a.part_ml + prow * 2) =
+            f32x2{l_tot > 0.f ? w.mref : -INFINITY, l_tot};
+    }
+    return;
   }
 
   // ---- epilogue: normalise, store O (bf16) and LSE (natural log) ----
@@ -652,21 +688,87 @@ __device__ __forceinline__ void fwd_pair_body(const FwdArgs& a) {
   if (!lwave) store_rows(qw);
 }
 
+// Merges the key-range splits of each query row: M = max m_s, L = sum l_s 2^(m_s - M),
+// O = sum O_s 2^(m_s - M) / L (the online-softmax merge), then O in bf16 and the natural-log
+// LSE. D/4 threads per row, each with 4 consecutive columns.
+template <int D>
+__device__ __forceinline__ void fwd_split_combine_body(const FwdArgs& a) {
+  constexpr int TPR = D / 4;
+  const size_t nrows = (size_t)a.B * a.Hq * a.Sq;
+  const size_t row = (size_t)blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
+  const int c4 = (threadIdx.x % TPR) * 4;
+  if (row >= nrows) return;
+  float M = -INFINITY;
+  for (int s = 0; s < a.nsplit; ++s) M = fmaxf(M, a.part_ml[((size_t)s * nrows + row) * 2]);
+  float L = 0.f;
+  f32x4 O = f32x4{};
+  if (M != -INFINITY) {
+    for (int s = 0; s < a.nsplit; ++s) {
+      const size_t pr = (size_t)s * nrows + row;
+      const f32x2 ml = *reinterpret_cast<const f32x2*>(a.part_ml + pr * 2);
+      if (ml[0] == -INFINITY) continue;
+      const float wgt = exp2_fast(ml[0] - M);
+      L += wgt * ml[1];
+      O += wgt * *reinterpret_cast<const f32x4*>(a.part_o + pr * D + c4);
+    }
+  }
+  const float inv = (L > 0.f) ? 1.f / L : 0.f;
+  u32x2 v = {pack_bf16x2(O[0] * inv, O[1] * inv), pack_bf16x2(O[2] * inv, O[3] * inv)};
+  *reinterpret_cast<u32x2*>(a.o + row * D + c4) = v;
+  if (a.lse != nullptr && c4 == 0)
+    a.lse[row] = (L > 0.f) ? (M + log2_fast(L)) * kLn2 : -INFINITY;
+}
+
+template <int D, bool CAUSAL>
+__device__ __forceinline__ void fwd_tile_full(const FwdArgs& a) { fwd_tile_body<D, CAUSAL, false>(a); }
+template <int D, bool CAUSAL>
+__device__ __forceinline__ void fwd_tile_split(const FwdArgs& a) { fwd_tile_body<D, CAUSAL, true>(a); }
+
 // Plain kernels (not kernel templates): their host-side launch stubs then depend only on these
 // signatures.
 #define ATTN_FWD_KERNEL(NAME, BODY, WAVES, D, CAUSAL)                      \
   __global__ __launch_bounds__(64 * WAVES)                                 \
   __attribute__((amdgpu_waves_per_eu(2, 2)))                               \
   void NAME(FwdArgs a) { BODY<D, CAUSAL>(a); }
-ATTN_FWD_KERNEL(fwd_bf16_d128_causal, fwd_tile_body, 4, 128, true)
-ATTN_FWD_KERNEL(fwd_bf16_d128, fwd_tile_body, 4, 128, false)
-ATTN_FWD_KERNEL(fwd_bf16_d64_causal, fwd_tile_body, 4, 64, true)
-ATTN_FWD_KERNEL(fwd_bf16_d64, fwd_tile_body, 4, 64, false)
+ATTN_FWD_KERNEL(fwd_bf16_d128_causal, fwd_tile_full, 4, 128, true)
+ATTN_FWD_KERNEL(fwd_bf16_d128, fwd_tile_full, 4, 128, false)
+ATTN_FWD_KERNEL(fwd_bf16_d64_causal, fwd_tile_full, 4, 64, true)
+ATTN_FWD_KERNEL(fwd_bf16_d64, fwd_tile_full, 4, 64, false)
+ATTN_FWD_KERNEL(fwd_bf16_d128_causal_split, fwd_tile_split, 4, 128, true)
+ATTN_FWD_KERNEL(fwd_bf16_d128_split, fwd_tile_split, 4, 128, false)
+ATTN_FWD_KERNEL(fwd_bf16_d64_causal_split, fwd_tile_split, 4, 64, true)
+ATTN_FWD_KERNEL(fwd_bf16_d64_split, fwd_tile_split, 4, 64, false)
 ATTN_FWD_KERNEL(fwd_bf16_d128_causal_pairs, fwd_pair_body, 8, 128, true)
 ATTN_FWD_KERNEL(fwd_bf16_d64_causal_pairs, fwd_pair_body, 8, 64, true)
 #undef ATTN_FWD_KERNEL
 
+__global__ __launch_bounds__(256) void fwd_bf16_d128_split_combine(FwdArgs a) {
+  fwd_split_combine_body<128>(a);
+}
+__global__ __launch_bounds__(256) void fwd_bf16_d64_split_combine(FwdArgs a) {
+  fwd_split_combine_body<64>(a);
+}
+
 }  // namespace
+
+int fwd_bf16_splits(const FwdProblem& p, int cus) {
+  const long long ntq = (p.Sq + kBM - 1) / kBM;
+  const long long items = ntq * p.B * p.Hq;
+  if (items <= 0 || items * 2 >= 3LL * cus) return 1;   // enough query tiles to fill the chip
+  // key tiles of the heaviest query tile; at least four per split
+  const int kv = p.causal ? std::min(p.Sk, std::max(0, (int)ntq * kBM + p.Sk - p.Sq)) : p.Sk;
+  const int tmax = (kv + kBN - 1) / kBN;
+  long long s = (2LL * cus + items - 1) / items;
+  s = std::min<long long>(s, kMaxFwdSplits);
+  s = std::min<long long>(s, std::max(1, tmax / 4));
+  return (int)std::max<long long>(s, 1);
+}
+
+size_t fwd_bf16_workspace_bytes(const FwdProblem& p, int nsplit) {
+  if (nsplit <= 1) return 0;
+  const size_t rows = (size_t)nsplit * p.B * p.Hq * p.Sq;
+  return rows * p.D * sizeof(float) + rows * 2 * sizeof(float);
+}
 
 hipError_t launch_fwd_bf16(const FwdProblem& p, hipStream_t stream) {
   FwdArgs a;
@@ -684,6 +786,31 @@ hipError_t launch_fwd_bf16(const FwdProblem& p, hipStream_t stream) {
   // argument rounds to 0) while keeping -inf * c = -inf for masked keys.
   if (!(c > 0.f)) c = 1.17549435e-38f;
   a.c = c;
+  a.nsplit = p.nsplit > 1 ? p.nsplit : 1;
+  a.part_o = nullptr;
+  a.part_ml = nullptr;
+  if (a.nsplit > 1) {
+    const size_t rows = (size_t)a.nsplit * p.B * p.Hq * p.Sq;
+    a.part_o = static_cast<float*>(p.workspace);
+    a.part_ml = a.part_o + rows * p.D;
+    const long long nwg = (long long)a.ntq * a.nsplit * p.B * p.Hq;
+    if (nwg == 0) return hipSuccess;
+    if (nwg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    dim3 grid((unsigned)nwg), block(256);
+    const size_t nrows = (size_t)p.B * p.Hq * p.Sq;
+    const int rows_per_block = 256 / (p.D / 4);
+    dim3 cgrid((unsigned)((nrows + rows_per_block - 1) / rows_per_block)), cblock(256);
+    if (p.D == 128) {
+      if (p.causal) hipLaunchKernelGGL(fwd_bf16_d128_causal_split, grid, block, 0, stream, a);
+      else hipLaunchKernelGGL(fwd_bf16_d128_split, grid, block, 0, stream, a);
+      hipLaunchKernelGGL(fwd_bf16_d128_split_combine, cgrid, cblock, 0, stream, a);
+    } else {
+      if (p.causal) hipLaunchKernelGGL(fwd_bf16_d64_causal_split, grid, block, 0, stream, a);
+      else hipLaunchKernelGGL(fwd_bf16_d64_split, grid, block, 0, stream, a);
+      hipLaunchKernelGGL(fwd_bf16_d64_split_combine, cgrid, cblock, 0, stream, a);
+    }
+    return hipGetLastError();
+  }
   const bool pairs = p.causal && a.ntq <= kPairMaxTiles;
   const long long nwg = (long long)(pairs ? a.npairs : a.ntq) * p.B * p.Hq;
   if (nwg == 0) return hipSuccess;

@@ -17,8 +17,14 @@ struct FwdProblem {
   int B, Hq, Hkv, Sq, Sk, D;
   int causal;
   float scale;
+  int nsplit;        // bf16: key-range splits per query tile (<= 1: none)
+  void* workspace;   // bf16 with nsplit > 1: fwd_bf16_workspace_bytes(p, nsplit) bytes
 };
 
+// Key-range splits the bf16 forward uses on a device with cus compute units (1 when the
+// query tiles alone fill it), and the workspace bytes those splits need.
+int fwd_bf16_splits(const FwdProblem& p, int cus);
+size_t fwd_bf16_workspace_bytes(const FwdProblem& p, int nsplit);
 // bf16 Q/K/V/O, fp32 LSE; MFMA kernel. D in {64, 128}.
 hipError_t launch_fwd_bf16(const FwdProblem& p, hipStream_t stream);
 // fp32 Q/K/V/O, fp32 LSE; vector-ALU kernel. D in {64, 128}.

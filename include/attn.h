@@ -51,18 +51,37 @@ enum attn_status {
                                 pointer not 4-byte aligned */
   ATTN_ERR_SCALE = 5,        /* scale is NaN, infinite or negative */
   ATTN_ERR_HIP = 6,          /* the HIP runtime reported an error (text in attn_last_error) */
-  ATTN_ERR_NOMEM = 7,        /* the decode workspace could not be allocated */
-  ATTN_ERR_WORKSPACE = 8     /* caller workspace too small or misaligned */
+  ATTN_ERR_NOMEM = 7,        /* the library workspace could not be allocated */
+  ATTN_ERR_WORKSPACE = 8     /* caller workspace too small or misaligned, or the library
+                                workspace would have to grow during graph capture */
 };
 
 /* Prefill / full-sequence forward, bfloat16 q, k, v, o (float32 lse).
  * lse may be NULL (not written). Layouts and semantics as above. D in {64, 128}.
- * One head's K (and V) must be under 2 GiB: Sk * D * 2 < 2^31, else ATTN_ERR_SHAPE. */
+ * One head's K (and V) must be under 2 GiB: Sk * D * 2 < 2^31, else ATTN_ERR_SHAPE.
+ * When B * Hq * ceil(Sq / 128) query tiles are too few to fill the device (a short query
+ * chunk against a long prefix, say), each tile's keys are split into up to 8 ranges whose
+ * partial results are merged by a second kernel (the same online-softmax merge), through a
+ * library-owned workspace: one per (device, stream), grown on demand (growing synchronises
+ * the device and is refused with ATTN_ERR_WORKSPACE while the stream is being captured into
+ * a graph). attn_fwd_ex takes a caller workspace instead. */
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              int B, int Hq, int Hkv, int Sq, int Sk, int D,
              int causal, float scale, void* stream);
 
-/* The same computation with float32 q, k, v, o (full-precision path). */
+/* attn_fwd with a caller-owned workspace for the key-range splits: at least
+ * attn_fwd_workspace_bytes(B, Hq, Hkv, Sq, Sk, D, causal) bytes, 16-byte aligned
+ * (ATTN_ERR_WORKSPACE otherwise); NULL = the library workspace. Calls sharing one workspace
+ * must not overlap in time. For callers that capture graphs. */
+int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+                int B, int Hq, int Hkv, int Sq, int Sk, int D, int causal, float scale,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes attn_fwd / attn_fwd_ex need on the current device for this problem
+ * (0 when it runs without key-range splits or the arguments are invalid). */
+size_t attn_fwd_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk, int D, int causal);
+
+/* The same computation with float32 q, k, v, o (full-precision path; no workspace). */
 int attn_fwd_f32(const void* q, const void* k, const void* v, void* o, float* lse,
                  int B, int Hq, int Hkv, int Sq, int Sk, int D,
                  int causal, float scale, void* stream);
@@ -176,7 +195,7 @@ const char* attn_last_error(void);
 /* Frees the library-owned decode workspaces (synchronises the devices that hold them). */
 void attn_release_workspace(void);
 
-/* ABI version of this header: 5. */
+/* ABI version of this header: 6. */
 int attn_abi_version(void);
 
 #ifdef __cplusplus

@@ -42,7 +42,7 @@ def test_status_strings_and_version():
     for code in range(9):
         assert A.attn_status_string(code) not in ("", "unknown status")
     assert A.attn_status_string(99) == "unknown status"
-    assert A.attn_abi_version() == 5
+    assert A.attn_abi_version() == 6
 
 
 def fwd(*, q=P, k=P, v=P, o=P, lse=0, B=1, Hq=32, Hkv=8, Sq=128, Sk=128, D=128, causal=1,
@@ -213,3 +213,17 @@ def test_rope_empty_and_sequence_map():
     assert rope(T=0, q=0, k=0, v=0, qo=0, kc=0, vc=0, table=0, pos=0) == OK
     # with a sequence map, more tokens than table rows is fine (the check is per token)
     assert rope(T=9, nseq=4, seq=P, q=0) == NULL
+
+
+def test_fwd_ex_workspace_checks():
+    lib = A.load_library()
+    need = A.attn_fwd_workspace_bytes(1, 32, 8, 512, 4096, 128, True)
+    # a 512-query chunk over 4096 keys has 128 query tiles: its key ranges are split
+    assert need > 0
+    assert A.attn_fwd_workspace_bytes(1, 32, 8, 2048, 2048, 128, True) == 0
+    assert A.attn_fwd_workspace_bytes(1, 32, 8, 512, 4096, 96, True) == 0
+    args = (P, P, P, P, 0, 1, 32, 8, 512, 4096, 128, 1, 0.08)
+    assert lib.attn_fwd_ex(*args, P, need - 1, None) == WS
+    assert lib.attn_fwd_ex(*args, P + 8, need, None) == WS
+    assert lib.attn_fwd_ex(P, P, P, P, 0, 1, 32, 8, 512, 4096, 96, 1, 0.08, P, need,
+                           None) == UNSUP

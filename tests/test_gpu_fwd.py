@@ -105,6 +105,18 @@ def test_config_llama3_8b_prefill_full(dev):
     print(f"llama3_8b_prefill: O max {mx:.3e} mean {mn:.3e}; LSE max {err:.3e}")
 
 
+def test_config_chunked_prefill_full(dev):
+    """A chunked-prefill step: the last 512 of 4096 tokens (Hq=32, Hkv=8, D=128, bf16)
+    against the whole prefix, bottom-right causal: every output element."""
+    cfg = W.CONFIGS["chunked_prefill_512_of_4096"]
+    q, k, v = W.fwd_inputs_for(cfg)
+    o, lse = run_bf16(q, k, v, cfg.causal, cfg.scale, dev)
+    O, L = oracle.attention(q, k, v, causal=cfg.causal, scale=cfg.scale)
+    mx, mn = check_bf16(o, O)
+    err = check_lse(lse, L)
+    print(f"chunked_prefill_512_of_4096: O max {mx:.3e} mean {mn:.3e}; LSE max {err:.3e}")
+
+
 def _full_size_check(name, dev, nrows=384):
     cfg = W.CONFIGS[name]
     q, k, v = W.fwd_inputs_for(cfg)
@@ -208,3 +220,20 @@ def test_causal_row0_is_v0(dev):
     o, lse = A.attn_fwd(qg, kg, vg, causal=True)
     torch.cuda.synchronize()
     assert torch.equal(o[:, :, 0], vg.repeat_interleave(2, 1)[:, :, 0])
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Sq,Sk,causal", [
+    (2, 32, 8, 768, 300, False),   # 384 query tiles: one pass over the keys per tile
+    (1, 8, 2, 768, 300, False),    # 48 query tiles: key ranges split, then merged
+    (2, 32, 8, 768, 2000, True),
+    (1, 4, 4, 300, 5000, True),    # a short chunk over a long prefix, heavily split
+])
+def test_key_split_and_whole_paths(B, Hq, Hkv, Sq, Sk, causal, dev):
+    """The forward splits each query tile's keys when the tiles alone cannot fill the device;
+    both the split and the whole-range paths match the oracle, with and without the mask."""
+    q, k, v = W.fwd_inputs(B, Hq, Hkv, Sq, Sk, 128, seed=B * 1000 + Sq + Sk)
+    scale = np.float32(1 / np.sqrt(128))
+    o, lse = run_bf16(q, k, v, causal, scale, dev)
+    O, L = oracle.attention(q, k, v, causal=causal, scale=scale)
+    check_bf16(o, O)
+    check_lse(lse, L)

@@ -14,6 +14,9 @@ Workload shapes follow the pages:
   * the 32K-token case is the T x T score matrix of more than a billion entries in
     "Optimizing Large Language Model Inference Through Kernel Fusion and Advanced Memory
     Management", §FlashAttention and the Memory-Efficiency Revolution;
+  * the chunked prefill (the §8(f) N3 step) splits a prompt into chunks that each attend to
+    everything before them; prefill and decode as different schedules of one equation are in
+    "Kernel Fusion, Softmax, and Attention", fifth paragraph;
   * the paged decode layout (fixed-size blocks, a block table mapping a sequence's logical
     blocks to physical ones) is the one in §Paged Attention and Dynamic KV Cache Management
     of that same article;
@@ -119,6 +122,11 @@ CONFIGS = {
                                      block_size=16, ctx_lo=512, ctx_hi=4096, seed=1004),
     "long_s32768": FwdConfig("long_s32768", B=1, Hq=32, Hkv=8, Sq=32768, Sk=32768, D=128,
                              dtype="bf16", causal=True, seed=1005, input_scale=0.5),
+    # a prefill chunk: the last 512 tokens of a 4096-token prompt attend to the whole prefix
+    # (bottom-right causal), as a chunked prefill step does
+    "chunked_prefill_512_of_4096": FwdConfig("chunked_prefill_512_of_4096", B=1, Hq=32, Hkv=8,
+                                             Sq=512, Sk=4096, D=128, dtype="bf16",
+                                             causal=True, seed=1009),
 }
 
 

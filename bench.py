@@ -177,7 +177,7 @@ def norm_timing(A, torch, dev, flush, flush_sink, stream, reps):
         ev = HipEvents(2 * reps)
         for i in range(reps):
             if flush is not None:
-                torch.sum(flush, dim=0, dtype=torch.int64, out=flush_sink[0])
+                torch.amax(flush, dim=0, out=flush_sink)
             ev.record(2 * i, stream)
             A.add_rms_norm(gx, gr, gw, eps=cfg.eps, out=out, residual_out=tres)
             ev.record(2 * i + 1, stream)
@@ -222,7 +222,7 @@ def rope_timing(A, torch, dev, dq, dkc, dvc, dbt, dctx, flush, flush_sink, strea
         ev = HipEvents(2 * reps)
         for i in range(reps):
             if flush is not None:
-                torch.sum(flush, dim=0, dtype=torch.int64, out=flush_sink[0])
+                torch.amax(flush, dim=0, out=flush_sink)
             ev.record(2 * i, stream)
             A.rope_cache_write(q, k, v, p, kc, vc, bt, seq_ids=seq, q_out=qo)
             ev.record(2 * i + 1, stream)
@@ -368,7 +368,7 @@ def main():
     # written scratch would leave dirty lines whose write-back then lands inside the decode.
     flush = torch.zeros((args.flush_mib << 20) // 4, dtype=torch.int32, device=dev) \
         if args.flush_mib > 0 else None
-    flush_sink = torch.zeros(1, dtype=torch.int64, device=dev)
+    flush_sink = torch.zeros((), dtype=torch.int32, device=dev)
 
     def step(i=None):
         # events e0 | prefill | e1 | cache flush | e2 | decode (stream + combine) | e3, all on
@@ -379,7 +379,7 @@ def main():
         if i is not None:
             ev.record(4 * i + 1, stream)
         if flush is not None:
-            torch.sum(flush, dim=0, dtype=torch.int64, out=flush_sink[0])
+            torch.amax(flush, dim=0, out=flush_sink)
         if i is not None:
             ev.record(4 * i + 2, stream)
         A.attn_decode_paged(dq, dkc, dvc, dbt, dctx, scale=scale_d, out=do)

@@ -19,8 +19,9 @@
 //    key tiles, last tile first. At the end each L wave hands its partial softmax state to the
 //    H wave with the same rows through LDS, where the two are merged with the online-softmax
 //    rescaling. Every workgroup then does about the same work. Work items of one KV head are
-//    placed on one XCD so they share its L2, and the L waves raise their issue priority around
-//    their matrix-core work so the two waves of a SIMD drift out of step.
+//    placed on one XCD so they share its L2. Each wave software-pipelines its 32-key blocks
+//    (scores of one block, softmax of the previous, product with V of the one before, in one
+//    stretch of code) and the L waves issue all the direct loads (see the pipelined pair body).
 //
 // Each wave works on the transposed problem so that the softmax runs inside each lane:
 //   S^T[key][q] = K[key][:] . Q[q][:]        (MFMA 32x32x16: A = K from LDS, B = Q^T in VGPRs)
@@ -133,6 +134,32 @@ struct TileDma {
       const int row = (wave * G::kIPW + i) * G::kRPI + rsub;
       koff[i] = row * G::kRow + ((pos ^ kswz<D>(row)) * 16);
       voff[i] = row * G::kRow + ((pos ^ vswz<D>(row)) * 16);
+    }
+  }
+
+  // This wave's share of one tensor's tile (K with rsrc rk and offsets koff, or V) at key kt;
+  // rows past Sk are clamped as in issue().
+  template <bool V>
+  __device__ __forceinline__ void issue_one(char* dst, int kt, int Sk) const {
+    const int tile_off = kt * G::kRow;
+    const int last = Sk - 1 - kt;
+    if (last >= kBN - 1) {
+#pragma unroll
+      for (int i = 0; i < G::kIPW; ++i) {
+        const int blk = wave * G::kIPW + i;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(V ? rv : rk, (lds_void*)(dst + blk * 1024), 16,
+                                                 V ? voff[i] : koff[i], tile_off, 0, 0);
+      }
+    } else {
+      asm volatile("");
+#pragma unroll
+      for (int i = 0; i < G::kIPW; ++i) {
+        const int blk = wave * G::kIPW + i;
+        const int row = blk * G::kRPI + lane / G::kCPR;
+        const uint32_t shift = row > last ? (uint32_t)((row - last) * G::kRow) : 0u;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(V ? rv : rk, (lds_void*)(dst + blk * 1024), 16,
+                                                 (V ? voff[i] : koff[i]) - shift, tile_off, 0, 0);
+      }
     }
   }
 
@@ -475,19 +502,169 @@ __device__ __forceinline__ void fwd_tile_body(const FwdArgs& a) {
   }
 }
 
+// ---- software-pipelined pair kernel ----
+// Each 32-key block of a wave's rows passes three phases: its scores S^T = K Q^T (matrix
+// cores), its softmax (vector ALU: max, exponentials, bf16 P^T) and its product O^T += V^T P^T
+// (matrix cores). Slot t runs the scores of block t, the softmax of block t-1 and the product
+// of block t-2: the three are independent, so the exponentials issue between the matrix-core
+// instructions of the same wave instead of after them (on gfx950 a wave's own interleaved
+// vector work hides under its matrix-core work far better than the other wave's does).
+// The two blocks of the key tile at step j are slots (j, 0) and (j, 1); both products in step
+// j are of tile j - 1, so a step reads K of tile j and V of tile j - 1, and the V tile is
+// loaded one step after its K tile, into the other stage.
+
+template <int D>
+struct Pipe {
+  f32x16 s;       // scores of the block waiting for its softmax
+  u32x4 pb[2];    // P^T (bf16) of the block waiting for its product with V
+  int s_k0;       // first key of the block in s
+  bool has_s;
+  bool has_p;
+  bool pv_b;      // the block in pb is from the second K/V stream
+};
+
+// Mask the block in p.s, take its row max and move the reference if needed (rescaling O, the
+// running sum and the P^T still waiting for its product, all relative to the old reference).
+// Returns the reference to subtract (0 while it is still -inf).
 template <int D, bool CAUSAL>
-__device__ __forceinline__ void fwd_pair_body(const FwdArgs& a) {
+__device__ __forceinline__ float pipe_prep(WaveState<D>& w, Pipe<D>& p, int Sk, int qw, int off,
+                                           int l32, int h, float c) {
+  using G = Geo<D, 4>;
+  const int k0 = p.s_k0;
+  const bool need_mask = (k0 + 32 > Sk) || (CAUSAL && k0 + 31 > qw + off);
+  if (need_mask) {
+    const int my_q = qw + l32;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = k0 + 8 * (r >> 2) + 4 * h + (r & 3);
+      bool vis = key < Sk;
+      if (CAUSAL) vis = vis && (key <= my_q + off);
+      p.s[r] = vis ? p.s[r] : -INFINITY;
+    }
+  }
+  // (a tree: three dependent steps instead of eight)
+  const float m0 = fmax3(p.s[0], p.s[1], p.s[2]), m1 = fmax3(p.s[3], p.s[4], p.s[5]);
+  const float m2 = fmax3(p.s[6], p.s[7], p.s[8]), m3 = fmax3(p.s[9], p.s[10], p.s[11]);
+  const float m4 = fmax3(p.s[12], p.s[13], p.s[14]);
+  float mx = fmax3(fmax3(m0, m1, m2), fmax3(m3, m4, p.s[15]), -INFINITY);
+  mx = xor32_max(mx);
+  const float mxc = mx * c;
+  const bool move = mxc > w.mref + kLazy;
+  if (__builtin_amdgcn_ballot_w64(move)) {
+    asm volatile("");
+    const float alpha = move ? exp2_fast(w.mref - mxc) : 1.f;
+    w.mref = move ? mxc : w.mref;
+    w.l_run *= alpha;
+#pragma unroll
+    for (int i = 0; i < G::DB; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) w.o[i][r] *= alpha;
+    if (p.has_p) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t u = p.pb[t][e];
+          p.pb[t][e] = pack_bf16x2(bf16lo_to_f32(u) * alpha, bf16hi_to_f32(u) * alpha);
+        }
+    }
+  }
+  return (w.mref == -INFINITY) ? 0.f : w.mref;
+}
+
+// One slot: with QK the scores of the 32-key block at kblk (K rows in LDS) into p.s; with EX the
+// softmax of the block in p.s (reference mu) into p.pb; with PV, O^T += V^T P^T for the block in
+// p.pb, whose V rows start at vblk. The matrix-core instructions of the scores and of the product
+// alternate, with one group of exponentials after each pair.
+template <int D, bool QK, bool EX, bool PV>
+__device__ __forceinline__ void pipe_slot(WaveState<D>& w, Pipe<D>& p, const char* kblk,
+                                          const char* vblk, float c, float mu) {
+  using G = Geo<D, 4>;
+  constexpr int KS = G::KS;            // score k-steps
+  constexpr int NP = 2 * G::DB;        // product instructions (as many as score k-steps)
+  static_assert(KS == NP, "one score and one product instruction per step");
+  constexpr int NM = KS;
+  // (a compiler barrier: the next slot's operand reads would otherwise be hoisted into this
+  //  one, which doubles the live fragments and undoes the schedule below)
+  asm volatile("" ::: "memory");
+  u32x4 kf[KS];
+  u32x4 vf[NP];
+  if (QK) {
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) kf[kk] = *reinterpret_cast<const u32x4*>(kblk + w.koff[kk]);
+  }
+  if (PV) {
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      const int db = i >> 1, t = i & 1;
+      const char* vp = vblk + w.voff[db] + 16 * t * G::kRow;
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vp));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vp + 8 * G::kRow));
+      const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
+      const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
+      vf[i] = u32x4{l2[0], l2[1], h2[0], h2[1]};
+    }
+  }
+  f32x16 sn;
+  u32x4 pn[2];
+  float ls0 = 0.f, ls1 = 0.f;
+  // the score products first, so that the next slot's max finds them complete; the products
+  // with V after them; the 8 exponential items spread over all of them
+  constexpr int NI = (QK ? NM : 0) + (PV ? NM : 0);
+#pragma unroll
+  for (int i = 0; i < (NI > 0 ? NI : 1); ++i) {
+    if (QK && i < NM) sn = mfma32x32x16(kf[i], w.qf[i], i == 0 ? f32x16{} : sn);
+    const int ip = QK ? i - NM : i;
+    if (PV && ip >= 0 && ip < NM) w.o[ip >> 1] = mfma32x32x16(vf[ip], p.pb[ip & 1], w.o[ip >> 1]);
+    if (EX) {
+#pragma unroll
+      for (int it = NI > 0 ? (8 * i) / NI : 0; it < (NI > 0 ? (8 * (i + 1)) / NI : 8); ++it) {
+        const int t = it >> 2, e = it & 3;
+        const float p0 = exp2_fast(__builtin_fmaf(p.s[8 * t + 2 * e], c, -mu));
+        const float p1 = exp2_fast(__builtin_fmaf(p.s[8 * t + 2 * e + 1], c, -mu));
+        ls0 += p0;
+        ls1 += p1;
+        pn[t][e] = pack_bf16x2(p0, p1);
+      }
+    }
+  }
+  if (EX) {
+    w.l_run += ls0 + ls1;
+    p.pb[0] = pn[0];
+    p.pb[1] = pn[1];
+  }
+  if (QK) p.s = sn;
+  // Schedule: every LDS operand read first (they complete in order while the first products
+  // run), then per step its matrix-core instructions followed by its vector work. (Group masks:
+  // 0x100 LDS read, 0x008 matrix core, 0x002 vector ALU.)
+  constexpr int NDS = (QK ? KS : 0) + (PV ? 2 * NP : 0);
+  // 7 vector instructions per exponential item (2 FMA, 2 exp, 2 adds, 1 pack): 56 over NI
+  // matrix-core instructions, alternately rounded down and up
+  __builtin_amdgcn_sched_group_barrier(0x100, NDS, 0);
+  constexpr int VA = NI > 0 ? (112 / NI + 1) / 2 : 0, VB = NI > 0 ? 112 / NI - VA : 0;
+#pragma unroll
+  for (int i = 0; i < NI; i += 2) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if (EX) __builtin_amdgcn_sched_group_barrier(0x002, VA, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if (EX) __builtin_amdgcn_sched_group_barrier(0x002, VB, 0);
+  }
+}
+
+template <int D, bool CAUSAL>
+__device__ __forceinline__ void fwd_pair_pipe_body(const FwdArgs& a) {
   using G = Geo<D, 8>;
-  // two K/V streams x two stages; separate objects so the compiler can tell the in-flight
-  // direct loads into one stage from the reads of another
-  __shared__ __attribute__((aligned(1024))) char ska0[G::kTile];
-  __shared__ __attribute__((aligned(1024))) char sva0[G::kTile];
-  __shared__ __attribute__((aligned(1024))) char ska1[G::kTile];
-  __shared__ __attribute__((aligned(1024))) char sva1[G::kTile];
-  __shared__ __attribute__((aligned(1024))) char skb0[G::kTile];
-  __shared__ __attribute__((aligned(1024))) char svb0[G::kTile];
-  __shared__ __attribute__((aligned(1024))) char skb1[G::kTile];
-  __shared__ __attribute__((aligned(1024))) char svb1[G::kTile];
+  // K stages k?0 / k?1 and V stages v?0 / v?1 of streams a and b; at step j the wave reads K
+  // stage j % 2 and V stage (j - 1) % 2 while K of step j + 1 and V of step j load into the
+  // other two (separate objects, so the compiler tells the in-flight direct loads apart)
+  __shared__ __attribute__((aligned(1024))) char ka0[G::kTile];
+  __shared__ __attribute__((aligned(1024))) char va0[G::kTile];
+  __shared__ __attribute__((aligned(1024))) char ka1[G::kTile];
+  __shared__ __attribute__((aligned(1024))) char va1[G::kTile];
+  __shared__ __attribute__((aligned(1024))) char kb0[G::kTile];
+  __shared__ __attribute__((aligned(1024))) char vb0[G::kTile];
+  __shared__ __attribute__((aligned(1024))) char kb1[G::kTile];
+  __shared__ __attribute__((aligned(1024))) char vb1[G::kTile];
   __shared__ float xml[4][2][64];     // hand-over of (mref, l_run) from the L waves
 
   const int tid = threadIdx.x;
@@ -495,10 +672,9 @@ __device__ __forceinline__ void fwd_pair_body(const FwdArgs& a) {
   const int wave = wave_uniform(tid >> 6);
   const int l32 = lane & 31;
   const int h = lane >> 5;
-  const bool lwave = wave < 4;           // L wave (light rows, then the heavy tail)
-  const int wr = wave & 3;               // 32-row block of a tile
+  const bool lwave = wave < 4;
+  const int wr = wave & 3;
 
-  // ---- work item ----
   const int item = xcd_item(blockIdx.x, a.nitems);
   const int pair = item % a.npairs;
   const int bh = item / a.npairs;
@@ -516,10 +692,9 @@ __device__ __forceinline__ void fwd_pair_body(const FwdArgs& a) {
     th = 2 * pair + 1;
     single = th >= a.ntq;
   }
-  if (single) th = tl;                   // the only tile is the heavy one; no light rows
-  const int off = a.Sk - a.Sq;           // causal diagonal offset
+  if (single) th = tl;
+  const int off = a.Sk - a.Sq;
 
-  // K/V tiles holding a key that some row of tile t sees
   auto tiles_for = [&](int t) -> int {
     const int last = min(t * kBM + kBM, a.Sq) - 1;
     int kend = a.Sk;
@@ -528,31 +703,27 @@ __device__ __forceinline__ void fwd_pair_body(const FwdArgs& a) {
   };
   const int nH = tiles_for(th);
   const int nL = single ? 0 : tiles_for(tl);
-  const int x = (nL + nH + 1) / 2;       // steps; the H waves take key tiles [0, x)
-  const int nB = nH - x;                 // key tiles [x, nH) of the heavy rows go to the L waves
+  const int x = (nL + nH + 1) / 2;       // steps with a key tile; step x only drains
+  const int nB = nH - x;
 
   const uint16_t* qbase = a.q + ((size_t)(b * a.Hq + hq) * a.Sq) * D;
   const uint16_t* kbase = a.k + ((size_t)(b * a.Hkv + hk) * a.Sk) * D;
   const uint16_t* vbase = a.v + ((size_t)(b * a.Hkv + hk) * a.Sk) * D;
 
   WaveState<D> w;
-  // K operand: row l32 (+32kb), chunk 2kk+h at its permuted slot
 #pragma unroll
   for (int kk = 0; kk < G::KS; ++kk)
     w.koff[kk] = l32 * G::kRow + (((2 * kk + h) ^ kswz<D>(l32)) * 16);
-  // V^T operand via transposed reads: source lane (group g, index j) points at key
-  // 4*(g/2) + j/4 (+ the block's first key) and columns 32db + 16*(g%2) + 4*(j%4) .. +3
   {
-    const int g = lane >> 4, j = lane & 15;
-    const int keyl = 4 * (g >> 1) + (j >> 2);
-    const int small = 2 * (g & 1) + ((j & 3) >> 1);
+    const int g = lane >> 4, jj = lane & 15;
+    const int keyl = 4 * (g >> 1) + (jj >> 2);
+    const int small = 2 * (g & 1) + ((jj & 3) >> 1);
 #pragma unroll
     for (int db = 0; db < G::DB; ++db)
-      w.voff[db] = keyl * G::kRow + (((4 * db + small) ^ vswz<D>(keyl)) * 16) + 8 * (j & 1);
+      w.voff[db] = keyl * G::kRow + (((4 * db + small) ^ vswz<D>(keyl)) * 16) + 8 * (jj & 1);
   }
   const float c = a.c;
 
-  // rows of the wave: qw .. qw + 31
   auto begin_rows = [&](int qw) {
     const int qi = qw + l32;
 #pragma unroll
@@ -562,8 +733,6 @@ __device__ __forceinline__ void fwd_pair_body(const FwdArgs& a) {
       else
         w.qf[kk] = u32x4{0, 0, 0, 0};
     }
-    // Consume the Q loads here: otherwise the loop's first use of qf must wait for every
-    // outstanding global load, including the next tile's prefetch.
 #pragma unroll
     for (int kk = 0; kk < G::KS; ++kk) asm volatile("" : "+v"(w.qf[kk]));
 #pragma unroll
@@ -571,7 +740,6 @@ __device__ __forceinline__ void fwd_pair_body(const FwdArgs& a) {
     w.mref = -INFINITY;
     w.l_run = 0.f;
   };
-  // normalise and store O (bf16) and LSE (natural log) of the rows qw .. qw + 31
   auto store_rows = [&](int qw) {
     const int my_q = qw + l32;
     const float l_tot = xor32_sum(w.l_run);
@@ -596,11 +764,11 @@ __device__ __forceinline__ void fwd_pair_body(const FwdArgs& a) {
 
   const int qlight = tl * kBM + 32 * wr;
   const int qheavy = th * kBM + 32 * wr;
-  int qw;                                 // rows the wave is working on
+  int qw;
   if (lwave && !single) {
     qw = qlight;
     begin_rows(qw);
-    if (nL == 0) {                        // light rows that see no key at all
+    if (nL == 0) {
       store_rows(qw);
       qw = qheavy;
       begin_rows(qw);
@@ -610,58 +778,102 @@ __device__ __forceinline__ void fwd_pair_body(const FwdArgs& a) {
     begin_rows(qw);
   }
 
-  TileDma<D, 8> dma;
-  dma.init(wave, lane, kbase, vbase, a.Sk);
-  // step j: stream A holds key tile j (H waves, and L waves while j < nL); stream B holds key
-  // tile nH + nL - 1 - j (L waves, once past their light rows: the heavy tail walked from its
-  // end, which with the causal pairing is tile 2T + 1 - j for every pair, so the workgroups
-  // running side by side read the same two tiles at each step and share them in L2)
-  auto prefetch = [&](int j, char* ska, char* sva, char* skb, char* svb) {
-    if (j >= x) return;
-    dma.issue(ska, sva, j * kBN, a.Sk);
-    if (j >= nL && j - nL < nB) dma.issue(skb, svb, (nH + nL - 1 - j) * kBN, a.Sk);
-  };
-  auto step = [&](int j, const char* ska, const char* sva, const char* skb, const char* svb) {
-    const char *sk, *sv;
-    int kt;
-    if (!lwave) {
-      sk = ska; sv = sva; kt = j * kBN;
-    } else if (j < nL) {
-      sk = ska; sv = sva; kt = j * kBN;
-    } else if (j - nL < nB) {
-      sk = skb; sv = svb; kt = (nH + nL - 1 - j) * kBN;
-    } else {
-      return;                             // this L wave has no tile at this step
-    }
-    const int wave_last_key = qw + 31 + off;   // last key any query of this wave may see
-    if (!CAUSAL || kt <= wave_last_key)
-      compute_tile<D, CAUSAL>(w, sk, sv, kt, a.Sk, qw, wave_last_key, qw + l32, off, h, c, lwave);
-    if (lwave && j == nL - 1) {           // light rows done: store them, move to the heavy tail
-      store_rows(qw);
-      if (nB > 0) {
-        qw = qheavy;
-        begin_rows(qw);
-      }
-    }
+  Pipe<D> p;
+  p.has_s = false;
+  p.has_p = false;
+  p.pv_b = false;
+  p.s_k0 = 0;
+
+  // The L waves issue all the direct loads: issued by all eight waves right after a barrier
+  // they queue behind each other for ~600 cycles, which the L waves (lighter per step) absorb
+  // while the H waves go straight to their matrix-core work.
+  TileDma<D, 4> dma;
+  dma.init(wr, lane, kbase, vbase, a.Sk);
+  // key tile of stream b at step j (the heavy rows' tail, walked from its end)
+  auto ktb = [&](int j) { return (nH + nL - 1 - j) * kBN; };
+  auto in_b = [&](int j) { return j >= nL && j - nL < nB; };
+  // loads started at step j: K of step j + 1 and V of step j
+  auto dma_step = [&](int j, char* kan, char* kbn, char* vac, char* vbc) {
+    if (!lwave) return;
+    if (j + 1 < x) dma.template issue_one<false>(kan, (j + 1) * kBN, a.Sk);
+    if (in_b(j + 1)) dma.template issue_one<false>(kbn, ktb(j + 1), a.Sk);
+    if (j < x) dma.template issue_one<true>(vac, j * kBN, a.Sk);
+    if (in_b(j)) dma.template issue_one<true>(vbc, ktb(j), a.Sk);
   };
 
-  prefetch(0, ska0, sva0, skb0, svb0);
+  // finishes the block pipeline of the current rows (V of the last key tile in vprev)
+  auto drain = [&](const char* vprev) {
+    if (!p.has_s) return;
+    const float mu = pipe_prep<D, CAUSAL>(w, p, a.Sk, qw, off, l32, h, c);
+    pipe_slot<D, false, true, true>(w, p, nullptr, vprev, c, mu);
+    pipe_slot<D, false, false, true>(w, p, nullptr, vprev + 32 * G::kRow, c, 0.f);
+    p.has_s = false;
+    p.has_p = false;
+  };
+
+  // the wave's work at step j: K of the step's tile in k{a,b}, V of the previous step's tile in
+  // v{a,b}
+  auto step = [&](int j, const char* kac, const char* kbc, const char* vap, const char* vbp) {
+    int kt = -1;
+    bool sb = false;
+    if (j < x) {
+      if (!lwave || j < nL) {
+        kt = j * kBN;
+      } else if (j - nL < nB) {
+        kt = ktb(j);
+        sb = true;
+      }
+    }
+    const bool row_switch = lwave && !single && nL > 0 && j == nL;
+    const int rows = row_switch ? qheavy : qw;
+    const bool vis = kt >= 0 && (!CAUSAL || kt <= rows + 31 + off);
+    if (p.has_s && (!vis || row_switch)) drain(p.pv_b ? vbp : vap);
+    if (row_switch) {
+      store_rows(qw);
+      qw = qheavy;
+      if (nB > 0) begin_rows(qw);
+    }
+    if (!vis) return;
+    const char* kt_lds = sb ? kbc : kac;
+    const char* vp = p.pv_b ? vbp : vap;
+    // slot (j, 0)
+    if (p.has_s) {
+      const float mu = pipe_prep<D, CAUSAL>(w, p, a.Sk, qw, off, l32, h, c);
+      pipe_slot<D, true, true, true>(w, p, kt_lds, vp, c, mu);
+    } else {
+      pipe_slot<D, true, false, false>(w, p, kt_lds, nullptr, c, 0.f);
+    }
+    const bool had_p = p.has_s;          // a P^T of the previous tile is now waiting
+    p.s_k0 = kt;
+    p.has_s = true;
+    // slot (j, 1)
+    {
+      const float mu = pipe_prep<D, CAUSAL>(w, p, a.Sk, qw, off, l32, h, c);
+      if (had_p)
+        pipe_slot<D, true, true, true>(w, p, kt_lds + 32 * G::kRow, vp + 32 * G::kRow, c, mu);
+      else
+        pipe_slot<D, true, true, false>(w, p, kt_lds + 32 * G::kRow, nullptr, c, mu);
+    }
+    p.s_k0 = kt + 32;
+    p.has_p = true;
+    p.pv_b = sb;
+  };
+
+  if (lwave && x > 0) dma.template issue_one<false>(ka0, 0, a.Sk);
+  if (lwave && in_b(0)) dma.template issue_one<false>(kb0, ktb(0), a.Sk);
   wait_dma_and_barrier();
-  for (int j = 0; j < x; j += 2) {
-    // stage 0 holds step j; prefetch step j+1 into stage 1
-    prefetch(j + 1, ska1, sva1, skb1, svb1);
-    step(j, ska0, sva0, skb0, svb0);
+  for (int j = 0; j <= x; j += 2) {
+    dma_step(j, ka1, kb1, va0, vb0);
+    step(j, ka0, kb0, va1, vb1);
     wait_dma_and_barrier();
-    if (j + 1 >= x) break;
-    prefetch(j + 2, ska0, sva0, skb0, svb0);
-    step(j + 1, ska1, sva1, skb1, svb1);
+    if (j + 1 > x) break;
+    dma_step(j + 1, ka0, kb0, va1, vb1);
+    step(j + 1, ka1, kb1, va0, vb0);
     wait_dma_and_barrier();
   }
 
-  // ---- merge the heavy rows' two partial states, store ----
   if (nB > 0) {
-    // (every stage is free after the loop's final barrier)
-    float* xo = reinterpret_cast<float*>(wr == 0 ? ska0 : wr == 1 ? sva0 : wr == 2 ? ska1 : sva1);
+    float* xo = reinterpret_cast<float*>(wr == 0 ? ka0 : wr == 1 ? va0 : wr == 2 ? ka1 : va1);
     if (lwave) {
 #pragma unroll
       for (int db = 0; db < G::DB; ++db)
@@ -738,8 +950,8 @@ ATTN_FWD_KERNEL(fwd_bf16_d128_causal_split, fwd_tile_split, 4, 128, true)
 ATTN_FWD_KERNEL(fwd_bf16_d128_split, fwd_tile_split, 4, 128, false)
 ATTN_FWD_KERNEL(fwd_bf16_d64_causal_split, fwd_tile_split, 4, 64, true)
 ATTN_FWD_KERNEL(fwd_bf16_d64_split, fwd_tile_split, 4, 64, false)
-ATTN_FWD_KERNEL(fwd_bf16_d128_causal_pairs, fwd_pair_body, 8, 128, true)
-ATTN_FWD_KERNEL(fwd_bf16_d64_causal_pairs, fwd_pair_body, 8, 64, true)
+ATTN_FWD_KERNEL(fwd_bf16_d128_causal_pairs, fwd_pair_pipe_body, 8, 128, true)
+ATTN_FWD_KERNEL(fwd_bf16_d64_causal_pairs, fwd_pair_pipe_body, 8, 64, true)
 #undef ATTN_FWD_KERNEL
 
 __global__ __launch_bounds__(256) void fwd_bf16_d128_split_combine(FwdArgs a) {

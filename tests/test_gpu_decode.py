@@ -152,6 +152,26 @@ def test_decode_zero_context_and_caller_workspace(dev):
     assert bool((o[[0, 2]] == 0).all())
 
 
+def test_decode_caller_workspace_reuse(dev):
+    """One caller workspace serves calls of different shapes and worker counts in turn: each
+    result equals the library-workspace call bit for bit and the oracle within the bar."""
+    ws = torch.empty(A.attn_decode_workspace_bytes(64, 32, 8, 128, 5000), dtype=torch.uint8,
+                     device=dev)
+    cases = [(8, 32, 8, 128, 768), (64, 32, 8, 128, 37), (3, 8, 2, 64, 5000),
+             (64, 32, 8, 128, 0), (16, 16, 1, 128, 2), (5, 8, 8, 64, 1)]
+    for i, (B, Hq, Hkv, D, wk) in enumerate(cases):
+        d = W.decode_inputs(B=B, Hq=Hq, Hkv=Hkv, D=D, block_size=16, ctx_lo=0, ctx_hi=700,
+                            seed=70 + i)
+        q, kc, vc, bt, cl = upload(d, dev)
+        o, lse = A.attn_decode_paged_ex(q, kc, vc, bt, cl, num_workers=wk, workspace=ws)
+        o2, lse2 = A.attn_decode_paged_ex(q, kc, vc, bt, cl, num_workers=wk)
+        torch.cuda.synchronize()
+        assert torch.equal(o, o2) and torch.equal(lse, lse2), f"case {i}"
+        O, L = oracle.decode_paged(d.q, d.k_cache, d.v_cache, d.block_table, d.ctx_lens, 16)
+        check_bf16(to_np(o), O)
+        check_lse(to_np(lse), L)
+
+
 def test_decode_is_deterministic(dev):
     d = W.decode_inputs(B=16, Hq=32, Hkv=8, D=128, block_size=16, ctx_lo=500, ctx_hi=3000,
                         seed=10)

@@ -137,46 +137,19 @@ struct TileDma {
     }
   }
 
-  // This wave's share of one tensor's tile (K with rsrc rk and offsets koff, or V) at key kt;
-  // rows past Sk are clamped as in issue().
-  template <bool V>
-  __device__ __forceinline__ void issue_one(char* dst, int kt, int Sk) const {
-    const int tile_off = kt * G::kRow;
-    const int last = Sk - 1 - kt;
-    if (last >= kBN - 1) {
-#pragma unroll
-      for (int i = 0; i < G::kIPW; ++i) {
-        const int blk = wave * G::kIPW + i;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(V ? rv : rk, (lds_void*)(dst + blk * 1024), 16,
-                                                 V ? voff[i] : koff[i], tile_off, 0, 0);
-      }
-    } else {
-      asm volatile("");
-#pragma unroll
-      for (int i = 0; i < G::kIPW; ++i) {
-        const int blk = wave * G::kIPW + i;
-        const int row = blk * G::kRPI + lane / G::kCPR;
-        const uint32_t shift = row > last ? (uint32_t)((row - last) * G::kRow) : 0u;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(V ? rv : rk, (lds_void*)(dst + blk * 1024), 16,
-                                                 (V ? voff[i] : koff[i]) - shift, tile_off, 0, 0);
-      }
-    }
-  }
-
-  // Issue this wave's share of the loads of the tile at key kt. A tile that runs past Sk
-  // clamps those keys to Sk-1: they are masked out of the scores, and their (finite) V rows
-  // are multiplied by a probability of exactly 0.
-  __device__ __forceinline__ void issue(char* sk, char* sv, int kt, int Sk) const {
+  // This wave's share of the loads of one tensor's tile (K through rk and koff, or V) at key
+  // kt. A tile that runs past Sk clamps those keys to Sk-1: they are masked out of the scores,
+  // and their (finite) V rows are multiplied by a probability of exactly 0.
+  // (v is a constant at every call site; inlining folds the selection)
+  __device__ __forceinline__ void issue_one(bool v, char* dst, int kt, int Sk) const {
     const int tile_off = kt * G::kRow;
     const int last = Sk - 1 - kt;                 // last valid row of this tile
     if (last >= kBN - 1) {
 #pragma unroll
       for (int i = 0; i < G::kIPW; ++i) {
         const int blk = wave * G::kIPW + i;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(sk + blk * 1024), 16, koff[i],
-                                                 tile_off, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(sv + blk * 1024), 16, voff[i],
-                                                 tile_off, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(v ? rv : rk, (lds_void*)(dst + blk * 1024), 16,
+                                                 v ? voff[i] : koff[i], tile_off, 0, 0);
       }
     } else {
       // (the empty asm keeps this a branch: folded into straight-line code, the clamping
@@ -187,12 +160,16 @@ struct TileDma {
         const int blk = wave * G::kIPW + i;
         const int row = blk * G::kRPI + lane / G::kCPR;
         const uint32_t shift = row > last ? (uint32_t)((row - last) * G::kRow) : 0u;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(sk + blk * 1024), 16,
-                                                 koff[i] - shift, tile_off, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(sv + blk * 1024), 16,
-                                                 voff[i] - shift, tile_off, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(v ? rv : rk, (lds_void*)(dst + blk * 1024), 16,
+                                                 (v ? voff[i] : koff[i]) - shift, tile_off, 0, 0);
       }
     }
+  }
+
+  // both tensors' tiles at key kt
+  __device__ __forceinline__ void issue(char* sk, char* sv, int kt, int Sk) const {
+    issue_one(false, sk, kt, Sk);
+    issue_one(true, sv, kt, Sk);
   }
 };
 
@@ -253,14 +230,13 @@ __device__ __forceinline__ void pv_blocks(WaveState<D>& w, const char* sv,
 template <int D, bool CAUSAL>
 __device__ __forceinline__ void compute_tile(WaveState<D>& w, const char* sk, const char* sv,
                                              int kt, int Sk, int qw, int wave_last_key,
-                                             int my_q, int off, int h, float c, bool lead) {
+                                             int my_q, int off, int h, float c) {
   using G = Geo<D, 4>;
   bool act[2];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
     act[kb] = (kt + 32 * kb < Sk) && (!CAUSAL || kt + 32 * kb <= wave_last_key);
 
-  if (lead) __builtin_amdgcn_s_setprio(2);
   // ---- S^T = K Q^T ----
   // (computed for every block: a block no query of this wave can see is masked below, and
   //  skipping it would cost a register copy of every score on all the other tiles)
@@ -278,7 +254,6 @@ __device__ __forceinline__ void compute_tile(WaveState<D>& w, const char* sk, co
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32x32x16(kf[kb][kk], w.qf[kk], s[kb]);
 
-  if (lead) __builtin_amdgcn_s_setprio(0);
   // ---- mask: causal diagonal, key tail, inactive blocks ----
   const bool need_mask = (kt + kBN > Sk) || (CAUSAL && kt + kBN - 1 > qw + off);
   if (need_mask) {
@@ -342,9 +317,7 @@ __device__ __forceinline__ void compute_tile(WaveState<D>& w, const char* sk, co
   w.l_run += ls[0] + ls[1];
 
   // ---- O^T += V^T P^T over the active 32-key blocks (a uniform choice per tile) ----
-  if (lead) __builtin_amdgcn_s_setprio(2);
   pv_blocks<D, 2>(w, sv, pb);
-  if (lead) __builtin_amdgcn_s_setprio(0);
 }
 
 // Work item -> (batch, query head, pair). Workgroups are dispatched to the 8 XCDs round
@@ -449,13 +422,12 @@ __device__ __forceinline__ void fwd_tile_body(const FwdArgs& a) {
     const int kt = (t0 + j) * kBN;
     // stage 0 holds tile j; prefetch tile j+1 into stage 1
     if (j + 1 < ntiles) dma.issue(sk1, sv1, kt + kBN, a.Sk);
-    compute_tile<D, CAUSAL>(w, sk0, sv0, kt, a.Sk, qw, wave_last_key, my_q, off, h, c, false);
+    compute_tile<D, CAUSAL>(w, sk0, sv0, kt, a.Sk, qw, wave_last_key, my_q, off, h, c);
     wait_dma_and_barrier();
     if (j + 1 >= ntiles) break;
     // stage 1 holds tile j+1; prefetch tile j+2 into stage 0
     if (j + 2 < ntiles) dma.issue(sk0, sv0, kt + 2 * kBN, a.Sk);
-    compute_tile<D, CAUSAL>(w, sk1, sv1, kt + kBN, a.Sk, qw, wave_last_key, my_q, off, h, c,
-                            false);
+    compute_tile<D, CAUSAL>(w, sk1, sv1, kt + kBN, a.Sk, qw, wave_last_key, my_q, off, h, c);
     wait_dma_and_barrier();
   }
 
@@ -795,10 +767,10 @@ __device__ __forceinline__ void fwd_pair_pipe_body(const FwdArgs& a) {
   // loads started at step j: K of step j + 1 and V of step j
   auto dma_step = [&](int j, char* kan, char* kbn, char* vac, char* vbc) {
     if (!lwave) return;
-    if (j + 1 < x) dma.template issue_one<false>(kan, (j + 1) * kBN, a.Sk);
-    if (in_b(j + 1)) dma.template issue_one<false>(kbn, ktb(j + 1), a.Sk);
-    if (j < x) dma.template issue_one<true>(vac, j * kBN, a.Sk);
-    if (in_b(j)) dma.template issue_one<true>(vbc, ktb(j), a.Sk);
+    if (j + 1 < x) dma.issue_one(false, kan, (j + 1) * kBN, a.Sk);
+    if (in_b(j + 1)) dma.issue_one(false, kbn, ktb(j + 1), a.Sk);
+    if (j < x) dma.issue_one(true, vac, j * kBN, a.Sk);
+    if (in_b(j)) dma.issue_one(true, vbc, ktb(j), a.Sk);
   };
 
   // finishes the block pipeline of the current rows (V of the last key tile in vprev)
@@ -859,8 +831,8 @@ __device__ __forceinline__ void fwd_pair_pipe_body(const FwdArgs& a) {
     p.pv_b = sb;
   };
 
-  if (lwave && x > 0) dma.template issue_one<false>(ka0, 0, a.Sk);
-  if (lwave && in_b(0)) dma.template issue_one<false>(kb0, ktb(0), a.Sk);
+  if (lwave && x > 0) dma.issue_one(false, ka0, 0, a.Sk);
+  if (lwave && in_b(0)) dma.issue_one(false, kb0, ktb(0), a.Sk);
   wait_dma_and_barrier();
   for (int j = 0; j <= x; j += 2) {
     dma_step(j, ka1, kb1, va0, vb0);

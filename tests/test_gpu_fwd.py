@@ -67,6 +67,32 @@ def test_fwd_bf16_small(shape, dev):
     check_lse(lse, L)
 
 
+def random_pair_shape(seed):
+    """A causal shape in the paired-tile kernel's range (at most 64 query tiles per head),
+    drawn from a seeded generator: odd and even tile counts, Sq above or below Sk (positive and
+    negative diagonal offsets), ragged tails, D = 64 or 128, GQA 1:1 to 4:1."""
+    rng = np.random.default_rng(500 + seed)
+    B = int(rng.integers(1, 3))
+    Hkv = int(rng.integers(1, 3))
+    Hq = Hkv * int(rng.choice([1, 2, 4]))
+    D = int(rng.choice([64, 128]))
+    Sq = int(rng.integers(1, 1600))
+    Sk = int(rng.integers(1, 1600))
+    return B, Hq, Hkv, Sq, Sk, D
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_fwd_pair_kernel_random_shapes(seed, dev):
+    B, Hq, Hkv, Sq, Sk, D = random_pair_shape(seed)
+    q, k, v = W.fwd_inputs(B, Hq, Hkv, Sq, Sk, D, seed=900 + seed)
+    scale = np.float32(1 / np.sqrt(D))
+    o, lse = run_bf16(q, k, v, True, scale, dev)
+    O, L = oracle.attention(q, k, v, causal=True, scale=scale)
+    what = f"B={B} Hq={Hq} Hkv={Hkv} Sq={Sq} Sk={Sk} D={D}"
+    check_bf16(o, O, what=what + " O")
+    check_lse(lse, L, what=what + " LSE")
+
+
 @pytest.mark.parametrize("shape", [(1, 1, 1, 128, 128, 64, False), (2, 4, 2, 200, 150, 128, True),
                                    (1, 2, 1, 77, 300, 64, True), (1, 2, 2, 300, 90, 128, True)],
                          ids=lambda s: "x".join(map(str, s)))

@@ -93,6 +93,37 @@ def test_fwd_pair_kernel_random_shapes(seed, dev):
     check_lse(lse, L, what=what + " LSE")
 
 
+def random_split_shape(seed):
+    """Seeds 0-6: few query tiles against up to 3000 keys, causal or not -- calls with fewer
+    query tiles than the CUs can take split their key ranges (a second kernel merges the
+    ranges). Seeds 7-9: enough query tiles (B=2, 16 heads, ~1600 rows) for the one-range-per-
+    tile kernel, non-causal."""
+    rng = np.random.default_rng(700 + seed)
+    if seed >= 7:
+        return (2, 16, 4, int(rng.integers(1536, 1800)), int(rng.integers(100, 1200)),
+                int(rng.choice([64, 128])), False)
+    B = int(rng.integers(1, 3))
+    Hkv = int(rng.integers(1, 3))
+    Hq = Hkv * int(rng.choice([1, 2, 4]))
+    D = int(rng.choice([64, 128]))
+    Sq = int(rng.integers(1, 700))
+    Sk = int(rng.integers(1, 3000))
+    causal = bool(rng.integers(0, 2))
+    return B, Hq, Hkv, Sq, Sk, D, causal
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_fwd_split_and_tile_random_shapes(seed, dev):
+    B, Hq, Hkv, Sq, Sk, D, causal = random_split_shape(seed)
+    q, k, v = W.fwd_inputs(B, Hq, Hkv, Sq, Sk, D, seed=1100 + seed)
+    scale = np.float32(1 / np.sqrt(D))
+    o, lse = run_bf16(q, k, v, causal, scale, dev)
+    O, L = oracle.attention(q, k, v, causal=causal, scale=scale)
+    what = f"B={B} Hq={Hq} Hkv={Hkv} Sq={Sq} Sk={Sk} D={D} causal={causal}"
+    check_bf16(o, O, what=what + " O")
+    check_lse(lse, L, what=what + " LSE")
+
+
 @pytest.mark.parametrize("shape", [(1, 1, 1, 128, 128, 64, False), (2, 4, 2, 200, 150, 128, True),
                                    (1, 2, 1, 77, 300, 64, True), (1, 2, 2, 300, 90, 128, True)],
                          ids=lambda s: "x".join(map(str, s)))

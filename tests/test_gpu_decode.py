@@ -172,6 +172,30 @@ def test_decode_caller_workspace_reuse(dev):
         check_lse(to_np(lse), L)
 
 
+@pytest.mark.parametrize("seed", range(10))
+def test_decode_random_shapes(seed, dev):
+    """Seeded random batches: 1-100 sequences, GQA 1:1 to 16:1, D = 64 or 128, context lengths
+    from a mix of empty, short and long (up to 3000) sequences, and a random worker count."""
+    rng = np.random.default_rng(1300 + seed)
+    B = int(rng.integers(1, 101))
+    Hkv = int(rng.choice([1, 2, 4, 8]))
+    Hq = Hkv * int(rng.choice([1, 2, 4, 8, 16]))
+    D = int(rng.choice([64, 128]))
+    kind = rng.integers(0, 3, size=B)
+    ctx = np.where(kind == 0, 0, np.where(kind == 1, rng.integers(1, 40, size=B),
+                                          rng.integers(40, 3001, size=B))).astype(np.int32)
+    workers = int(rng.choice([0, int(rng.integers(1, 2000))]))
+    d = W.decode_inputs(B=B, Hq=Hq, Hkv=Hkv, D=D, block_size=16, ctx_lo=0, ctx_hi=3000,
+                        seed=1400 + seed, ctx_lens=ctx)
+    q, kc, vc, bt, cl = upload(d, dev)
+    o, lse = A.attn_decode_paged_ex(q, kc, vc, bt, cl, num_workers=workers)
+    torch.cuda.synchronize()
+    O, L = oracle.decode_paged(d.q, d.k_cache, d.v_cache, d.block_table, d.ctx_lens, 16)
+    what = f"B={B} Hq={Hq} Hkv={Hkv} D={D} workers={workers}"
+    check_bf16(to_np(o), O, what=what + " O")
+    check_lse(to_np(lse), L, what=what + " LSE")
+
+
 def test_decode_is_deterministic(dev):
     d = W.decode_inputs(B=16, Hq=32, Hkv=8, D=128, block_size=16, ctx_lo=500, ctx_hi=3000,
                         seed=10)

@@ -61,14 +61,8 @@ __global__ __launch_bounds__(kRopeThreads) void rope_cache_kernel(RopeArgs a) {
   const int t = blockIdx.x;
   const int tid = threadIdx.x;
   const int p = a.pos[t];
-
-  if (tid < H2) {
-    const double theta = pow(a.base, -2.0 * (double)tid / (double)D);
-    double s, c;
-    sincos((double)p * theta, &s, &c);
-    cs[tid] = (float)c;
-    sn[tid] = (float)s;
-  }
+  const int nq = a.Hq * VP, nk = a.Hkv * VP;
+  const int nitems = nq + 2 * nk;
 
   // the cache row of this token (null when nothing is stored)
   size_t row = 0;
@@ -79,32 +73,71 @@ __global__ __launch_bounds__(kRopeThreads) void rope_cache_kernel(RopeArgs a) {
     store = a.num_blocks <= 0 || (phys >= 0 && phys < a.num_blocks);
     row = ((size_t)phys * a.Hkv) * kRopeBS * D + (size_t)(p % kRopeBS) * D;
   }
+
+  // item it: vectors j and j + D/16 of a query, key or value head
+  auto src_of = [&](int it, int& j) -> const uint16_t* {
+    if (it < nq) {
+      j = it % VP;
+      return a.q + ((size_t)t * a.Hq + it / VP) * D;
+    }
+    const int kv = it - nq;
+    const bool isv = kv >= nk;
+    const int w = isv ? kv - nk : kv;
+    j = w % VP;
+    return (isv ? a.v : a.k) + ((size_t)t * a.Hkv + w / VP) * D;
+  };
+  // the first two items' loads go out before the table and before any store, so that each
+  // thread keeps four 16-byte loads in flight
+  u32x4 lo0 = u32x4{0, 0, 0, 0}, hi0 = u32x4{0, 0, 0, 0};
+  u32x4 lo1 = u32x4{0, 0, 0, 0}, hi1 = u32x4{0, 0, 0, 0};
+  if (tid < nitems) {
+    int j;
+    const uint16_t* src = src_of(tid, j);
+    lo0 = *reinterpret_cast<const u32x4*>(src + 8 * j);
+    hi0 = *reinterpret_cast<const u32x4*>(src + H2 + 8 * j);
+  }
+  if (tid + kRopeThreads < nitems) {
+    int j;
+    const uint16_t* src = src_of(tid + kRopeThreads, j);
+    lo1 = *reinterpret_cast<const u32x4*>(src + 8 * j);
+    hi1 = *reinterpret_cast<const u32x4*>(src + H2 + 8 * j);
+  }
+
+  if (tid < H2) {
+    const double theta = pow(a.base, -2.0 * (double)tid / (double)D);
+    double sd, cd;
+    sincos((double)p * theta, &sd, &cd);
+    cs[tid] = (float)cd;
+    sn[tid] = (float)sd;
+  }
   __syncthreads();
 
-  const int nq = a.Hq * VP, nk = a.Hkv * VP;
-  for (int it = tid; it < nq + 2 * nk; it += kRopeThreads) {
-    int h, j;
-    const uint16_t* src;
+  for (int it = tid; it < nitems; it += kRopeThreads) {
+    int j;
+    const uint16_t* src = src_of(it, j);
+    u32x4 lo, hi;
+    if (it == tid) {
+      lo = lo0;
+      hi = hi0;
+    } else if (it == tid + kRopeThreads) {
+      lo = lo1;
+      hi = hi1;
+    } else {
+      lo = *reinterpret_cast<const u32x4*>(src + 8 * j);
+      hi = *reinterpret_cast<const u32x4*>(src + H2 + 8 * j);
+    }
     uint16_t* dst;
     bool rotate = true;
     if (it < nq) {
-      h = it / VP;
-      j = it % VP;
-      src = a.q + ((size_t)t * a.Hq + h) * D;
-      dst = a.q_out + ((size_t)t * a.Hq + h) * D;
+      dst = a.q_out + ((size_t)t * a.Hq + it / VP) * D;
     } else {
+      if (!store) continue;
       const int kv = it - nq;
       const bool isv = kv >= nk;
       const int w = isv ? kv - nk : kv;
-      h = w / VP;
-      j = w % VP;
-      if (!store) continue;
-      src = (isv ? a.v : a.k) + ((size_t)t * a.Hkv + h) * D;
-      dst = (isv ? a.vc : a.kc) + row + (size_t)h * kRopeBS * D;
+      dst = (isv ? a.vc : a.kc) + row + (size_t)(w / VP) * kRopeBS * D;
       rotate = !isv;
     }
-    const u32x4 lo = *reinterpret_cast<const u32x4*>(src + 8 * j);
-    const u32x4 hi = *reinterpret_cast<const u32x4*>(src + H2 + 8 * j);
     if (!rotate) {
       *reinterpret_cast<u32x4*>(dst + 8 * j) = lo;
       *reinterpret_cast<u32x4*>(dst + H2 + 8 * j) = hi;

@@ -47,10 +47,11 @@ SMALL = [
     (1, 2, 2, 1, 777, 128, True),         # one query, a decode-like row
     (1, 2, 2, 70, 1, 128, False),         # one key
     (3, 2, 1, 129, 63, 64, False),        # Sk below one tile
-    (1, 4, 4, 512, 512, 128, True),       # several full tiles, MHA
-    # causal launches with few tiles per head take the paired-tile kernel
-    (1, 2, 1, 1100, 1100, 128, True),     # 9 tiles: four pairs and one tile on its own
-    (1, 2, 1, 900, 400, 128, True),       # Sq > Sk: whole light tiles see no key
+    (1, 4, 4, 512, 512, 128, True),       # several full tiles, MHA (key-range splits)
+    # with this few query tiles, causal calls split their key ranges when there are enough key
+    # tiles (the first, third and fourth here) and run the paired-tile kernel otherwise
+    (1, 2, 1, 1100, 1100, 128, True),     # 9 tiles
+    (1, 2, 1, 900, 400, 128, True),       # Sq > Sk: whole light tiles see no key (paired)
     (1, 8, 2, 1000, 1000, 64, True),      # D = 64, GQA 4:1
     (2, 2, 2, 640, 700, 128, True),       # Sq < Sk, ragged heavy tail
 ]
@@ -68,29 +69,39 @@ def test_fwd_bf16_small(shape, dev):
 
 
 def random_pair_shape(seed):
-    """A causal shape in the paired-tile kernel's range (at most 64 query tiles per head),
-    drawn from a seeded generator: odd and even tile counts, Sq above or below Sk (positive and
-    negative diagonal offsets), ragged tails, D = 64 or 128, GQA 1:1 to 4:1."""
+    """A causal shape that runs the paired-tile kernel: at most 64 query tiles per head and
+    enough query tiles in all (B * Hq * tiles >= 1.5 x the CUs) that the call does not split
+    its key ranges. Drawn from a seeded generator: odd and even tile counts, Sq above or below
+    Sk (both signs of the diagonal offset), ragged tails, D = 64 or 128, GQA 1:1 to 4:1."""
     rng = np.random.default_rng(500 + seed)
-    B = int(rng.integers(1, 3))
-    Hkv = int(rng.integers(1, 3))
+    B = int(rng.choice([4, 8]))
+    Hkv = int(rng.choice([4, 8]))
     Hq = Hkv * int(rng.choice([1, 2, 4]))
     D = int(rng.choice([64, 128]))
-    Sq = int(rng.integers(1, 1600))
-    Sk = int(rng.integers(1, 1600))
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    min_tiles = -(-3 * cus // (2 * B * Hq))          # ceil(1.5 CUs / (B Hq))
+    Sq = int(rng.integers(128 * (min_tiles - 1) + 1, 128 * (min_tiles + 3) + 1))
+    Sk = int(rng.integers(1, 2 * Sq + 64))
     return B, Hq, Hkv, Sq, Sk, D
 
 
 @pytest.mark.parametrize("seed", range(12))
 def test_fwd_pair_kernel_random_shapes(seed, dev):
+    """Sampled rows (every query tile's first and last rows among them) against the oracle."""
     B, Hq, Hkv, Sq, Sk, D = random_pair_shape(seed)
+    ntq = -(-Sq // 128)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert ntq <= 64 and 2 * B * Hq * ntq >= 3 * cus     # the paired-tile kernel runs
     q, k, v = W.fwd_inputs(B, Hq, Hkv, Sq, Sk, D, seed=900 + seed)
     scale = np.float32(1 / np.sqrt(D))
     o, lse = run_bf16(q, k, v, True, scale, dev)
-    O, L = oracle.attention(q, k, v, causal=True, scale=scale)
+    edges = [e for t in range(ntq) for e in (128 * t, 128 * t + 31, 128 * t + 32, 128 * t + 127)]
+    rows = W.sample_rows(B, Hq, Sq, 96 + len(edges), seed=seed, must=edges)
+    O, L = oracle.attention_rows(q, k, v, rows, causal=True, scale=scale)
+    idx = tuple(np.array(rows).T)
     what = f"B={B} Hq={Hq} Hkv={Hkv} Sq={Sq} Sk={Sk} D={D}"
-    check_bf16(o, O, what=what + " O")
-    check_lse(lse, L, what=what + " LSE")
+    check_bf16(o[idx], O, what=what + " sampled O")
+    check_lse(lse[idx], L, what=what + " sampled LSE")
 
 
 def random_split_shape(seed):
@@ -216,10 +227,13 @@ def test_causal_kernel_switch_sampled(ntiles, dev):
     """Causal launches with up to 64 query tiles of 128 rows per head run the paired-tile kernel,
     longer ones the one-tile-per-workgroup kernel; both sides of the switch, on sampled rows."""
     S = 128 * ntiles
-    q, k, v = W.fwd_inputs(1, 2, 1, S, S, 128, seed=1000 + ntiles)
+    # six query heads: 64 x 6 query tiles are enough that the call does not split key ranges
+    Hq = 6
+    assert 2 * Hq * ntiles >= 3 * torch.cuda.get_device_properties(0).multi_processor_count
+    q, k, v = W.fwd_inputs(1, Hq, 3, S, S, 128, seed=1000 + ntiles)
     o, lse = run_bf16(q, k, v, True, np.float32(1 / np.sqrt(128)), dev)
     edges = [0, 1, 127, 128, S // 2 - 1, S // 2, S // 2 + 127, S - 129, S - 128, S - 1]
-    rows = W.sample_rows(1, 2, S, 96, seed=ntiles, must=edges)
+    rows = W.sample_rows(1, Hq, S, 96, seed=ntiles, must=edges)
     O, L = oracle.attention_rows(q, k, v, rows, causal=True, scale=np.float32(1 / np.sqrt(128)))
     idx = tuple(np.array(rows).T)
     check_bf16(o[idx], O, what=f"{ntiles} tiles sampled O")

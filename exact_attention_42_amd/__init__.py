@@ -239,20 +239,16 @@ def _decode_checks(q, k_cache, v_cache, block_table, ctx_lens):
 
 def attn_decode_paged(q, k_cache, v_cache, block_table, ctx_lens, scale=None, out=None,
                       stream=None):
-    """Paged one-token decode (bf16). The block table's row stride is derived on the device
-    from ctx_lens, so ``block_table`` must be exactly [B, max_b ceil(ctx_b / block_size)]."""
-    torch = _torch()
-    B, Hq, D, nb, Hkv, bs, dev = _decode_checks(q, k_cache, v_cache, block_table, ctx_lens)
-    if out is None:
-        out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev)
-    _need(out, "out", torch.bfloat16, dev, (B, Hq, D))
-    if scale is None:
-        scale = 1.0 / math.sqrt(D)
-    with torch.cuda.device(dev):
-        _check(load_library().attn_decode_paged(
-            _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(ctx_lens), _ptr(out),
-            B, Hq, Hkv, D, bs, float(scale), _stream_ptr(dev, stream)))
-    return out
+    """Paged one-token decode (bf16); returns out [B, Hq, D].
+
+    Goes through the C entry point attn_decode_paged_ex with the block table's actual row
+    stride (``block_table.shape[1]``, which may exceed the longest context's block count, as
+    in a table preallocated for the maximum context) and the pool size ``k_cache.shape[0]``,
+    so a table entry outside the pool is skipped instead of read. (The 13-argument C entry
+    point attn_decode_paged derives the stride from ctx_lens instead.)"""
+    o, _ = attn_decode_paged_ex(q, k_cache, v_cache, block_table, ctx_lens, scale=scale,
+                                out=out, want_lse=False, stream=stream)
+    return o
 
 
 def attn_decode_paged_ex(q, k_cache, v_cache, block_table, ctx_lens, scale=None, out=None,

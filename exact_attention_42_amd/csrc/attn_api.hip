@@ -6,10 +6,13 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
+#include <cstring>
 #include <map>
 #include <mutex>
 #include <string>
 #include <utility>
+#include <vector>
+#include <algorithm>
 
 #include "attn.h"
 #include "kernels.hpp"
@@ -76,12 +79,24 @@ int check_fwd(const void* q, const void* k, const void* v, void* o, const float*
 
 // ---- workspace owned by the library: one buffer per (device, stream), shared by the decode's
 // partial results and the split forward's (calls on one stream run in order) ----
+//
+// Rules:
+//  * g_ws_mutex is held from the moment a call takes the library workspace until every kernel
+//    of that call is enqueued, so two host threads on one stream can never interleave their
+//    kernels over the same buffer;
+//  * a buffer that is replaced by a larger one is never freed while the library runs: it goes
+//    to g_retired and is freed, with the current ones, only by attn_release_workspace (kernels
+//    enqueued earlier may still read it);
+//  * the library workspace is refused on a stream that is being captured into a graph: the
+//    graph would keep its address while later eager calls replace the buffer. Graphs take a
+//    caller workspace through the _ex entry points.
 struct Workspace {
   void* ptr = nullptr;
   size_t bytes = 0;
 };
 std::mutex g_ws_mutex;
 std::map<std::pair<int, void*>, Workspace> g_ws;
+std::vector<std::pair<int, void*>> g_retired;   // (device, buffer) replaced by a larger one
 
 // Compute units of the current device (256 when it cannot be queried).
 int device_cus() {
@@ -110,34 +125,44 @@ int default_workers() {
   return w > kMaxWorkers ? kMaxWorkers : w;
 }
 
-int get_workspace(void* stream, size_t need, void** out) {
+// Forced work mapping of the bf16 forward: ATTN_FWD_MAPPING = "tile" or "pair" (for
+// measurement); unset or anything else = chosen per problem.
+int forced_fwd_mapping() {
+  static const int m = [] {
+    const char* s = std::getenv("ATTN_FWD_MAPPING");
+    if (!s) return -1;
+    if (std::strcmp(s, "tile") == 0) return (int)attn::kMapTile;
+    if (std::strcmp(s, "pair") == 0) return (int)attn::kMapPair;
+    return -1;
+  }();
+  return m;
+}
+
+// The library workspace of (current device, stream), at least need bytes. The caller must hold
+// g_ws_mutex until its kernels are enqueued.
+int get_workspace_locked(void* stream, size_t need, void** out) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
-  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(static_cast<hipStream_t>(stream), &cap) == hipSuccess &&
+      cap != hipStreamCaptureStatusNone)
+    return fail(ATTN_ERR_WORKSPACE, "this call needs %zu bytes of workspace on a stream that is "
+                "being captured into a graph; the library workspace is never used under "
+                "capture: pass a caller workspace through the _ex entry point", need);
+  (void)hipGetLastError();
   Workspace& w = g_ws[{dev, stream}];
   if (w.bytes < need) {
-    // growing allocates (and frees, which synchronises): not while a graph is being captured
-    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-    if (hipStreamIsCapturing(static_cast<hipStream_t>(stream), &cap) == hipSuccess &&
-        cap != hipStreamCaptureStatusNone)
-      return fail(ATTN_ERR_WORKSPACE, "this call needs %zu bytes of library workspace on a "
-                  "stream that is being captured; pass a caller workspace (the _ex entry "
-                  "points) or make the same call on this stream before capturing", need);
-    (void)hipGetLastError();
-    if (w.ptr) {
-      e = hipFree(w.ptr);   // synchronises: in-flight kernels may still read the old buffer
-      w.ptr = nullptr;
-      w.bytes = 0;
-      if (e != hipSuccess) return hip_fail(e, "hipFree(workspace)");
-    }
-    size_t sz = need < (1u << 20) ? (1u << 20) : need;
-    e = hipMalloc(&w.ptr, sz);
+    // grow geometrically, so the retired buffers add up to less than the live one
+    size_t sz = std::max(need, std::max(w.bytes * 2, (size_t)(1u << 20)));
+    void* p = nullptr;
+    e = hipMalloc(&p, sz);
     if (e != hipSuccess) {
-      w.ptr = nullptr;
       (void)hipGetLastError();
       return fail(ATTN_ERR_NOMEM, "workspace of %zu bytes: %s", sz, hipGetErrorString(e));
     }
+    if (w.ptr) g_retired.push_back({dev, w.ptr});
+    w.ptr = p;
     w.bytes = sz;
   }
   *out = w.ptr;
@@ -154,7 +179,9 @@ int run_fwd(bool f32, const void* q, const void* k, const void* v, void* o, floa
   if (!f32 && (long long)Sk * D * 2 > 0x7fffffffLL)
     return fail(ATTN_ERR_SHAPE, "Sk=%d too long for D=%d: Sk*D*2 must stay below 2^31", Sk, D);
   if (empty) return ok();
-  attn::FwdProblem p{q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, causal ? 1 : 0, scale, 1, nullptr};
+  attn::FwdProblem p{q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, causal ? 1 : 0, scale, 1, nullptr,
+                     forced_fwd_mapping()};
+  std::unique_lock<std::mutex> ws_lock(g_ws_mutex, std::defer_lock);
   if (!f32) {
     p.nsplit = attn::fwd_bf16_splits(p, device_cus());
     if (p.nsplit > 1) {
@@ -166,8 +193,9 @@ int run_fwd(bool f32, const void* q, const void* k, const void* v, void* o, floa
         if (!aligned(workspace, 16))
           return fail(ATTN_ERR_WORKSPACE, "workspace must be 16-byte aligned");
         p.workspace = workspace;
-      } else if (int rc = get_workspace(stream, need, &p.workspace)) {
-        return rc;
+      } else {
+        ws_lock.lock();
+        if (int rc = get_workspace_locked(stream, need, &p.workspace)) return rc;
       }
     }
   }
@@ -207,13 +235,15 @@ int run_decode(const void* q, const void* k_cache, const void* v_cache,
   const int workers = num_workers ? num_workers : default_workers();
   const size_t need = attn::decode_workspace_bytes(B, Hkv, Hq / Hkv, D, workers);
   void* ws = workspace;
+  std::unique_lock<std::mutex> ws_lock(g_ws_mutex, std::defer_lock);
   if (ws) {
     if (workspace_bytes < need)
       return fail(ATTN_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed",
                   workspace_bytes, need);
     if (!aligned(ws, 16)) return fail(ATTN_ERR_WORKSPACE, "workspace must be 16-byte aligned");
-  } else if (int rc = get_workspace(stream, need, &ws)) {
-    return rc;
+  } else {
+    ws_lock.lock();
+    if (int rc = get_workspace_locked(stream, need, &ws)) return rc;
   }
   attn::DecodeProblem p;
   p.q = q; p.k_cache = k_cache; p.v_cache = v_cache;
@@ -325,7 +355,7 @@ size_t attn_fwd_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk, int D, i
       (long long)B * Hq > 0x7fffffffLL || Sq > (1 << 30) || Sk > (1 << 30))
     return 0;
   attn::FwdProblem p{nullptr, nullptr, nullptr, nullptr, nullptr, B, Hq, Hkv, Sq, Sk, D,
-                     causal ? 1 : 0, 1.0f, 1, nullptr};
+                     causal ? 1 : 0, 1.0f, 1, nullptr, -1};
   return attn::fwd_bf16_workspace_bytes(p, attn::fwd_bf16_splits(p, device_cus()));
 }
 
@@ -382,7 +412,11 @@ void attn_release_workspace(void) {
       if (hipSetDevice(kv.first.first) == hipSuccess) (void)hipFree(kv.second.ptr);
     }
   }
+  for (auto& r : g_retired) {
+    if (hipSetDevice(r.first) == hipSuccess) (void)hipFree(r.second);
+  }
   g_ws.clear();
+  g_retired.clear();
   if (have_cur) (void)hipSetDevice(cur);
 }
 

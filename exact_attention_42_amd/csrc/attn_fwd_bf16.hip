@@ -948,6 +948,11 @@ int fwd_bf16_splits(const FwdProblem& p, int cus) {
   return (int)std::max<long long>(s, 1);
 }
 
+int fwd_bf16_mapping(const FwdProblem& p, int /*cus*/) {
+  const int ntq = (p.Sq + kBM - 1) / kBM;
+  return (p.causal && ntq <= kPairMaxTiles) ? kMapPair : kMapTile;
+}
+
 size_t fwd_bf16_workspace_bytes(const FwdProblem& p, int nsplit) {
   if (nsplit <= 1) return 0;
   const size_t rows = (size_t)nsplit * p.B * p.Hq * p.Sq;
@@ -995,7 +1000,7 @@ hipError_t launch_fwd_bf16(const FwdProblem& p, hipStream_t stream) {
     }
     return hipGetLastError();
   }
-  const bool pairs = p.causal && a.ntq <= kPairMaxTiles;
+  const bool pairs = (p.mapping >= 0 ? p.mapping : fwd_bf16_mapping(p, 256)) == kMapPair;
   const long long nwg = (long long)(pairs ? a.npairs : a.ntq) * p.B * p.Hq;
   if (nwg == 0) return hipSuccess;
   if (nwg > 0x7fffffffLL) return hipErrorInvalidConfiguration;

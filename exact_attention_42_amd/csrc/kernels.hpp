@@ -19,7 +19,14 @@ struct FwdProblem {
   float scale;
   int nsplit;        // bf16: key-range splits per query tile (<= 1: none)
   void* workspace;   // bf16 with nsplit > 1: fwd_bf16_workspace_bytes(p, nsplit) bytes
+  int mapping;       // bf16 without splits: FwdMapping, or -1 to choose by the problem
 };
+
+// Work mappings of the bf16 forward without key-range splits.
+enum FwdMapping { kMapTile = 0, kMapPair = 1 };
+
+// The mapping the bf16 forward uses for p (without key-range splits) when none is forced.
+int fwd_bf16_mapping(const FwdProblem& p, int cus);
 
 // Key-range splits the bf16 forward uses on a device with cus compute units (1 when the
 // query tiles alone fill it), and the workspace bytes those splits need.

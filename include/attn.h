@@ -31,6 +31,15 @@
  *     attn_last_error() returns on the calling thread.
  *   - B == 0, Sq == 0 (or, for decode, B == 0) is a valid empty problem: nothing is launched.
  *   - The calls are thread-safe.
+ *
+ * Library workspace. The split-KV decode, and the forward when it splits key ranges, keep
+ * partial results in device memory. Without a caller workspace (the _ex entry points) they use
+ * one owned by the library per (device, stream), allocated on first use and replaced by a
+ * larger one when a call needs more. A call holds it from taking it until all of its kernels
+ * are enqueued, so calls from several host threads on one stream never mix their partials.
+ * A replaced buffer is not freed until attn_release_workspace (kernels enqueued earlier may
+ * still read it). The library workspace is never used on a stream that is being captured into
+ * a graph: such a call returns ATTN_ERR_WORKSPACE; pass a caller workspace instead.
  */
 #ifndef EXACT_ATTENTION_ATTN_H
 #define EXACT_ATTENTION_ATTN_H
@@ -53,7 +62,7 @@ enum attn_status {
   ATTN_ERR_HIP = 6,          /* the HIP runtime reported an error (text in attn_last_error) */
   ATTN_ERR_NOMEM = 7,        /* the library workspace could not be allocated */
   ATTN_ERR_WORKSPACE = 8     /* caller workspace too small or misaligned, or the library
-                                workspace would have to grow during graph capture */
+                                workspace was needed on a stream under graph capture */
 };
 
 /* Prefill / full-sequence forward, bfloat16 q, k, v, o (float32 lse).
@@ -62,9 +71,8 @@ enum attn_status {
  * When B * Hq * ceil(Sq / 128) query tiles are too few to fill the device (a short query
  * chunk against a long prefix, say), each tile's keys are split into up to 8 ranges whose
  * partial results are merged by a second kernel (the same online-softmax merge), through a
- * library-owned workspace: one per (device, stream), grown on demand (growing synchronises
- * the device and is refused with ATTN_ERR_WORKSPACE while the stream is being captured into
- * a graph). attn_fwd_ex takes a caller workspace instead. */
+ * library-owned workspace (see "Library workspace" above). attn_fwd_ex takes a caller
+ * workspace instead. */
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              int B, int Hq, int Hkv, int Sq, int Sk, int D,
              int causal, float scale, void* stream);
@@ -100,8 +108,7 @@ int attn_fwd_f32(const void* q, const void* k, const void* v, void* o, float* ls
  * block_size must be 16. Hq / Hkv must be at most 16. The call runs two kernels on stream:
  * a streaming kernel in which W worker waves split the batch's (sequence, KV head, block)
  * list into equal contiguous shares and write partial results (running max, sum and
- * unnormalised output) to a library-owned workspace (one per device and stream, grown on
- * demand; growing it synchronises the device), and a combine kernel merging each sequence's
+ * unnormalised output) to the library workspace (see above), and a combine kernel merging each sequence's
  * partials with the running-softmax algebra. The caller must keep physical block ids valid;
  * they are not range-checked here (attn_decode_paged_ex can check them). */
 int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
@@ -192,7 +199,8 @@ const char* attn_status_string(int status);
 /* Detail of the last failed call on this thread ("" if none). */
 const char* attn_last_error(void);
 
-/* Frees the library-owned decode workspaces (synchronises the devices that hold them). */
+/* Frees every library-owned workspace, including replaced ones (synchronises the devices
+ * that hold them). No call may be running or enqueued-and-unfinished when it is called. */
 void attn_release_workspace(void);
 
 /* ABI version of this header: 6. */

@@ -106,7 +106,9 @@ def attention(q, k, v, causal=False, scale=None):
 def attention_rows(q, k, v, rows, causal=False, scale=None):
     """The same definition evaluated only at the listed (b, h, i) query rows.
 
-    Used to check full-size workloads whose complete output the CPU cannot afford.
+    Used to check full-size workloads whose complete output the CPU cannot afford. The rows
+    of one head are evaluated together (complete score rows, in slabs, exactly as in
+    ``attention``), so K and V of a head are widened to float64 once.
     Returns O [n, Dv] and LSE [n] in float64, in the order of ``rows``.
     """
     B, Hq, Sq, D = q.shape
@@ -117,13 +119,22 @@ def attention_rows(q, k, v, rows, causal=False, scale=None):
     g = Hq // Hkv
     outO = np.zeros((len(rows), v.shape[3]), dtype=np.float64)
     outL = np.zeros(len(rows), dtype=np.float64)
+    by_head = {}
     for n, (b, h, i) in enumerate(rows):
+        by_head.setdefault((int(b), int(h)), []).append((n, int(i)))
+    slab = max(1, _SLAB_BYTES // max(1, 8 * Sk))
+    for (b, h), items in by_head.items():
         hk = h // g
-        o, lse = _rows(q[b, h, i:i + 1].astype(np.float64), np.array([i]),
-                       k[b, hk].astype(np.float64), v[b, hk].astype(np.float64),
-                       causal, Sk - Sq, s)
-        outO[n] = o[0]
-        outL[n] = lse[0]
+        K = k[b, hk].astype(np.float64)
+        V = v[b, hk].astype(np.float64)
+        pos = np.array([n for n, _ in items])
+        idx = np.array([i for _, i in items])
+        for r0 in range(0, len(idx), slab):
+            r1 = min(len(idx), r0 + slab)
+            o, lse = _rows(q[b, h, idx[r0:r1]].astype(np.float64), idx[r0:r1], K, V, causal,
+                           Sk - Sq, s)
+            outO[pos[r0:r1]] = o
+            outL[pos[r0:r1]] = lse
     return outO, outL
 
 

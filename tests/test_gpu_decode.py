@@ -24,6 +24,22 @@ def upload(d, dev):
     return bf(d.q), bf(d.k_cache), bf(d.v_cache), i32(d.block_table), i32(d.ctx_lens)
 
 
+def plain_c_decode(q, kc, vc, bt, ctx, scale):
+    """The 13-argument C entry point attn_decode_paged, called directly: it derives the block
+    table's row stride on the device as max ceil(ctx / 16), so bt must have exactly that many
+    columns."""
+    import ctypes
+    B, Hq, D = q.shape
+    Hkv = kc.shape[1]
+    o = torch.empty_like(q)
+    p = lambda t: ctypes.c_void_p(t.data_ptr())
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    rc = A.load_library().attn_decode_paged(p(q), p(kc), p(vc), p(bt), p(ctx), p(o), B, Hq, Hkv,
+                                            D, 16, scale, stream)
+    assert rc == 0, A.attn_last_error()
+    return o
+
+
 def test_config_paged_decode_b64(dev):
     """B=64, Hq=32, Hkv=8, D=128, ctx uniform in [512, 4096], 16-token blocks placed by a
     seeded permutation, tail slots poisoned with 1e4: every output element."""
@@ -32,7 +48,9 @@ def test_config_paged_decode_b64(dev):
     q, kc, vc, bt, ctx = upload(d, dev)
     o = A.attn_decode_paged(q, kc, vc, bt, ctx, scale=float(cfg.scale))
     o2, lse = A.attn_decode_paged_ex(q, kc, vc, bt, ctx, scale=float(cfg.scale))
+    o3 = plain_c_decode(q, kc, vc, bt, ctx, float(cfg.scale))
     torch.cuda.synchronize()
+    assert torch.equal(o, o3)
     O, L = oracle.decode_paged(d.q, d.k_cache, d.v_cache, d.block_table, d.ctx_lens,
                                cfg.block_size, scale=cfg.scale)
     mx, mn = check_bf16(to_np(o), O)
@@ -204,3 +222,71 @@ def test_decode_is_deterministic(dev):
     for _ in range(30):
         o, l = A.attn_decode_paged_ex(q, kc, vc, bt, cl)
         assert torch.equal(o, ref) and torch.equal(l, ref_l)
+
+
+def test_decode_block_table_wider_than_the_contexts(dev):
+    """A block table preallocated wider than the longest context (as a serving loop keeps one
+    for the maximum length), with garbage past each sequence's blocks: the binding passes its
+    real row stride and the pool size, and the result matches the oracle."""
+    d = W.decode_inputs(B=6, Hq=16, Hkv=4, D=128, block_size=16, ctx_lo=1, ctx_hi=600, seed=44)
+    q, kc, vc, bt, cl = upload(d, dev)
+    wide = torch.full((6, bt.shape[1] * 3 + 5), 10 ** 6, dtype=torch.int32, device=dev)
+    wide[:, :bt.shape[1]] = bt
+    wide[:, :bt.shape[1]][bt < 0] = 10 ** 6
+    o = A.attn_decode_paged(q, kc, vc, wide, cl)
+    torch.cuda.synchronize()
+    O, L = oracle.decode_paged(d.q, d.k_cache, d.v_cache, d.block_table, d.ctx_lens, 16)
+    check_bf16(to_np(o), O)
+
+
+def test_library_workspace_two_threads_one_stream(dev):
+    """Two host threads share one stream and the library workspace, alternating problem sizes
+    so that the workspace is replaced by larger ones while the other thread's kernels may still
+    be queued: every result matches the oracle (a call holds the workspace until its kernels
+    are enqueued, and a replaced buffer stays allocated)."""
+    import threading
+    probs = []
+    for i, (B, ctx_hi) in enumerate([(2, 200), (24, 1500), (5, 900), (64, 4096)]):
+        d = W.decode_inputs(B=B, Hq=32, Hkv=8, D=128, block_size=16, ctx_lo=1, ctx_hi=ctx_hi,
+                            seed=600 + i)
+        O, L = oracle.decode_paged(d.q, d.k_cache, d.v_cache, d.block_table, d.ctx_lens, 16)
+        probs.append((upload(d, dev), O, L))
+    fq, fk, fv = W.fwd_inputs(1, 4, 2, 300, 3000, 128, seed=610)    # splits its key ranges
+    fO, fL = oracle.attention(fq, fk, fv, causal=True)
+    bf = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev).to(torch.bfloat16)
+    fgpu = (bf(fq), bf(fk), bf(fv))
+    torch.cuda.synchronize()
+    A.attn_release_workspace()
+    stream = torch.cuda.Stream()
+    results = [[], []]
+    errors = []
+
+    def worker(t):
+        try:
+            with torch.cuda.stream(stream):
+                for it in range(12):
+                    j = (it + 2 * t) % 5
+                    if j == 4:
+                        o, lse = A.attn_fwd(*fgpu, causal=True, stream=stream)
+                    else:
+                        (q, kc, vc, bt, cl), _, _ = probs[j]
+                        o, lse = A.attn_decode_paged_ex(q, kc, vc, bt, cl, stream=stream)
+                    results[t].append((j, o, lse))
+        except Exception as e:     # reported after the join
+            errors.append(e)
+
+    th = [threading.Thread(target=worker, args=(t,)) for t in range(2)]
+    for t in th:
+        t.start()
+    for t in th:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for t in range(2):
+        for j, o, lse in results[t]:
+            if j == 4:
+                check_bf16(to_np(o), fO, what=f"thread {t} prefill")
+                check_lse(to_np(lse), fL, what=f"thread {t} prefill LSE")
+            else:
+                check_bf16(to_np(o), probs[j][1], what=f"thread {t} decode {j}")
+                check_lse(to_np(lse), probs[j][2], what=f"thread {t} decode {j} LSE")

@@ -2,8 +2,10 @@
 fp64 oracle on identical seeded inputs (rounded to bf16 first for the bf16 path).
 
 Small shapes are compared element by element over every output and span several 128-query
-and 64-key tiles plus ragged tails; the full-size workloads are compared on sampled rows that
-the oracle computes one by one, and on properties that hold at any size.
+and 64-key tiles plus ragged tails. Of the full-size workloads, the Llama-3-8B-shaped prefill
+and the batched B=8, S=4096 one are compared on every element; the 32K-token one on one row
+of every 32-row slice of every head (every unit of work), and everywhere on properties that
+hold at any size.
 """
 import numpy as np
 import pytest
@@ -185,8 +187,18 @@ def test_config_chunked_prefill_full(dev):
     print(f"chunked_prefill_512_of_4096: O max {mx:.3e} mean {mn:.3e}; LSE max {err:.3e}")
 
 
-def _full_size_check(name, dev, nrows=384):
-    cfg = W.CONFIGS[name]
+def _oracle_threads(fn, jobs, threads=8):
+    """Runs independent oracle evaluations on a pool of host threads (numpy releases the GIL
+    in its kernels), each with a small BLAS thread count so the pool does not oversubscribe
+    the host."""
+    from concurrent.futures import ThreadPoolExecutor
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=2):
+        with ThreadPoolExecutor(max_workers=threads) as ex:
+            return list(ex.map(lambda j: fn(*j), jobs))
+
+
+def _run_full_size(cfg, dev):
     q, k, v = W.fwd_inputs_for(cfg)
     qg, kg, vg = (_gpu(x, dev, torch.bfloat16) for x in (q, k, v))
     o, lse = A.attn_fwd(qg, kg, vg, causal=cfg.causal, scale=float(cfg.scale))
@@ -198,28 +210,70 @@ def _full_size_check(name, dev, nrows=384):
     vmin = vg.float().amin(dim=2).repeat_interleave(g, dim=1)
     assert bool((o.float() <= vmax[:, :, None, :] + 2e-2).all())
     assert bool((o.float() >= vmin[:, :, None, :] - 2e-2).all())
-    # causal row 0 sees key 0 only: O = V_0 rounded, LSE = scale * q_0 . k_0
-    # sampled rows, including both sides of every tile edge that the samples touch
-    edges = [0, 1, 63, 64, 127, 128, 129, 255, 256, cfg.Sq - 129, cfg.Sq - 128, cfg.Sq - 2,
-             cfg.Sq - 1]
-    rows = W.sample_rows(cfg.B, cfg.Hq, cfg.Sq, nrows, seed=cfg.seed, must=edges)
-    O, L = oracle.attention_rows(q, k, v, rows, causal=cfg.causal, scale=cfg.scale)
+    # causal row 0 sees key 0 only: O = V_0 exactly (one weight of 1), LSE = scale q_0 . k_0
+    if cfg.causal and cfg.Sq == cfg.Sk:
+        assert torch.equal(o[:, :, 0], vg.repeat_interleave(g, dim=1)[:, :, 0])
+        s0 = np.float64(cfg.scale) * np.einsum(
+            "bhd,bhd->bh", q[:, :, 0].astype(np.float64),
+            np.repeat(k[:, :, 0], g, axis=1).astype(np.float64))
+        assert np.max(np.abs(lse[:, :, 0].cpu().numpy() - s0)) <= 1e-3
+    return q, k, v, o, lse
+
+
+def test_config_batched_b8_s4096_full(dev):
+    """B=8, H=32, S=4096, D=128, bf16, causal: every output element against the oracle (the
+    oracle runs batch entry by batch entry on a pool of host threads)."""
+    cfg = W.CONFIGS["batched_b8_s4096"]
+    q, k, v, o, lse = _run_full_size(cfg, dev)
+    res = _oracle_threads(
+        lambda b: oracle.attention(q[b:b + 1], k[b:b + 1], v[b:b + 1], causal=cfg.causal,
+                                   scale=cfg.scale), [(b,) for b in range(cfg.B)])
+    O = np.concatenate([r[0] for r in res])
+    L = np.concatenate([r[1] for r in res])
+    mx, mn = check_bf16(to_np(o), O, what="batched_b8_s4096 O")
+    err = check_lse(to_np(lse), L, what="batched_b8_s4096 LSE")
+    print(f"batched_b8_s4096: every element: O max {mx:.3e} mean {mn:.3e}; LSE max {err:.3e}")
+
+
+def test_config_long_s32768_every_wave_slice(dev):
+    """B=1, Hq=32, Hkv=8, S=32768, D=128, bf16 x0.5, causal: one row out of every 32-row slice
+    of every head (a seeded random row in each slice; 32,768 rows, every (head, 32-row) unit
+    of work), plus the last row of every head, against the oracle."""
+    cfg = W.CONFIGS["long_s32768"]
+    q, k, v, o, lse = _run_full_size(cfg, dev)
+    rng = np.random.default_rng(cfg.seed)
+    rows = []
+    for h in range(cfg.Hq):
+        picks = np.arange(0, cfg.Sq, 32) + rng.integers(0, 32, size=cfg.Sq // 32)
+        rows.extend((0, h, int(i)) for i in picks)
+        rows.append((0, h, cfg.Sq - 1))
+    heads = [[r for r in rows if r[1] == h] for h in range(cfg.Hq)]
+    res = _oracle_threads(
+        lambda rr: oracle.attention_rows(q, k, v, rr, causal=cfg.causal, scale=cfg.scale),
+        [(rr,) for rr in heads])
+    rows = [r for rr in heads for r in rr]
+    O = np.concatenate([r[0] for r in res])
+    L = np.concatenate([r[1] for r in res])
     idx = tuple(np.array(rows).T)
-    o_np = o.float().cpu().numpy()
-    lse_np = lse.cpu().numpy()
-    mx, mn = check_bf16(o_np[idx], O, what=f"{name} sampled O")
-    err = check_lse(lse_np[idx], L, what=f"{name} sampled LSE")
-    print(f"{name}: {len(rows)} rows: O max {mx:.3e} mean {mn:.3e}; LSE max {err:.3e}")
+    mx, mn = check_bf16(to_np(o)[idx], O, what="long_s32768 O (one row per 32-row slice)")
+    err = check_lse(to_np(lse)[idx], L, what="long_s32768 LSE")
+    print(f"long_s32768: {len(rows)} rows: O max {mx:.3e} mean {mn:.3e}; LSE max {err:.3e}")
 
 
-def test_config_batched_b8_s4096_sampled(dev):
-    """B=8, H=32, S=4096, D=128, bf16, causal at full size."""
-    _full_size_check("batched_b8_s4096", dev)
-
-
-def test_config_long_s32768_sampled(dev):
-    """B=1, Hq=32, Hkv=8, S=32768, D=128, bf16 x0.5, causal at full size."""
-    _full_size_check("long_s32768", dev, nrows=256)
+def test_long_causal_head_full(dev):
+    """A causal shape with more than 64 query tiles of 128 rows per head, enough work that the
+    keys are not split (B=1, Hq=6, Hkv=3, S=8320): every output element."""
+    q, k, v = W.fwd_inputs(1, 6, 3, 8320, 8320, 128, seed=8320)
+    scale = np.float32(1 / np.sqrt(128))
+    o, lse = run_bf16(q, k, v, True, scale, dev)
+    res = _oracle_threads(
+        lambda h: oracle.attention(q[:, h:h + 1], k[:, h // 2:h // 2 + 1],
+                                   v[:, h // 2:h // 2 + 1], causal=True, scale=scale),
+        [(h,) for h in range(6)])
+    O = np.concatenate([r[0] for r in res], axis=1)
+    L = np.concatenate([r[1] for r in res], axis=1)
+    mx, mn = check_bf16(o, O, what="S=8320 O")
+    check_lse(lse, L, what="S=8320 LSE")
 
 
 @pytest.mark.parametrize("ntiles", [64, 65])

@@ -49,13 +49,18 @@ def bf16_bits(x: np.ndarray) -> np.ndarray:
     bfloat16 become infinities, as IEEE rounding requires.
     """
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    lsb = (u >> 16) & 1
-    r = ((u + 0x7FFF + lsb) >> 16).astype(np.uint32)
+    u = x.view(np.uint32)
+    # u + 0x7FFF + lsb, in place in 32 bits: it cannot wrap for a finite value (the largest
+    # magnitude pattern 0xFF7FFFFF plus 0x8000 stays below 2^32); NaN patterns are redone below
+    r = (u >> 16) & 1
+    r += u
+    r += 0x7FFF
+    r >>= 16
+    r = r.astype(np.uint16)
     nan = np.isnan(x)
     if nan.any():
-        r = np.where(nan, ((u >> 16) | 0x40).astype(np.uint32), r)
-    return r.astype(np.uint16)
+        r[nan] = ((u[nan] >> 16) | 0x40).astype(np.uint16)
+    return r
 
 
 def bits_to_f32(b: np.ndarray) -> np.ndarray:

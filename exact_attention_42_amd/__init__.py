@@ -17,7 +17,7 @@ import os
 __all__ = [
     "AttnError", "library_path", "load_library",
     "attn_fwd", "attn_fwd_f32", "attn_fwd_ex", "attn_fwd_workspace_bytes", "attn_decode_paged",
-    "attn_decode_paged_ex",
+    "attn_decode_paged_ex", "attn_decode_paged_noalloc", "attn_decode_noalloc_max_bytes",
     "attn_decode_workspace_bytes", "attn_decode_default_workers", "attn_status_string",
     "attn_last_error", "attn_release_workspace", "attn_abi_version", "attn_add_rms_norm",
     "add_rms_norm", "attn_rope_cache_write", "rope_cache_write", "EXPORTED_SYMBOLS",
@@ -36,6 +36,9 @@ _SIGNATURES = {
     "attn_decode_paged": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P]),
     "attn_decode_paged_ex": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I,
                                   _I, _P, _Z, _P]),
+    "attn_decode_paged_noalloc": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F,
+                                       _I, _I, _I, _P]),
+    "attn_decode_noalloc_max_bytes": (_Z, []),
     "attn_decode_workspace_bytes": (_Z, [_I, _I, _I, _I, _I]),
     "attn_decode_default_workers": (_I, []),
     "attn_status_string": (ctypes.c_char_p, [_I]),
@@ -278,6 +281,35 @@ def attn_decode_paged_ex(q, k_cache, v_cache, block_table, ctx_lens, scale=None,
             _ptr(lse), B, Hq, Hkv, D, bs, float(scale), int(block_table.shape[1]),
             int(nb) if check_blocks else 0, int(num_workers), _ptr(workspace),
             int(workspace.numel()) if workspace is not None else 0, _stream_ptr(dev, stream)))
+    return out, lse
+
+
+def attn_decode_noalloc_max_bytes() -> int:
+    return load_library().attn_decode_noalloc_max_bytes()
+
+
+def attn_decode_paged_noalloc(q, k_cache, v_cache, block_table, ctx_lens, scale=None, out=None,
+                              lse=None, want_lse=True, check_blocks=True, num_workers=0,
+                              stream=None):
+    """Paged decode whose partial results live in the library's fixed device array (the C
+    entry point allocates nothing; ``out``/``lse`` are allocated here only when not given).
+    Returns (out, lse). Calls that overlap on one device race on that array."""
+    torch = _torch()
+    B, Hq, D, nb, Hkv, bs, dev = _decode_checks(q, k_cache, v_cache, block_table, ctx_lens)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev)
+    _need(out, "out", torch.bfloat16, dev, (B, Hq, D))
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, dev, (B, Hq))
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    with torch.cuda.device(dev):
+        _check(load_library().attn_decode_paged_noalloc(
+            _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(ctx_lens), _ptr(out),
+            _ptr(lse), B, Hq, Hkv, D, bs, float(scale), int(block_table.shape[1]),
+            int(nb) if check_blocks else 0, int(num_workers), _stream_ptr(dev, stream)))
     return out, lse
 
 

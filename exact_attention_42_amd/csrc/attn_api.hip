@@ -17,6 +17,14 @@
 #include "attn.h"
 #include "kernels.hpp"
 
+// Fixed device memory for attn_decode_paged_noalloc: the decode's partial results live here
+// instead of in an allocated workspace. Each device the library runs on holds its own copy
+// until the process ends. On the host `scratch` only names the symbol; its device address is
+// taken once per device with hipGetSymbolAddress (scratch_address below) and only that
+// address is ever passed to a kernel.
+constexpr size_t kScratchBytes = size_t(8) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -169,6 +177,34 @@ int get_workspace_locked(void* stream, size_t need, void** out) {
   return ATTN_OK;
 }
 
+// Device address of `scratch` on the current device, looked up once per device (with that
+// device current) and kept; a fixed table, so the lookup allocates nothing either.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(ATTN_ERR_UNSUPPORTED, "device %d: the fixed scratch supports devices 0..%d", dev,
+                kMaxDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr) {
+      (void)hipGetLastError();
+      return hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol,
+                      "hipGetSymbolAddress(scratch)");
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return ATTN_OK;
+}
+
 int run_fwd(bool f32, const void* q, const void* k, const void* v, void* o, float* lse, int B,
             int Hq, int Hkv, int Sq, int Sk, int D, int causal, float scale, void* workspace,
             size_t workspace_bytes, void* stream) {
@@ -209,7 +245,7 @@ int run_decode(const void* q, const void* k_cache, const void* v_cache,
                const int32_t* block_table, const int32_t* ctx_lens, void* o, float* lse, int B,
                int Hq, int Hkv, int D, int block_size, float scale, int table_stride,
                int num_blocks, int num_workers, void* workspace, size_t workspace_bytes,
-               void* stream) {
+               void* stream, bool use_scratch = false) {
   if (B < 0) return fail(ATTN_ERR_SHAPE, "B must be >= 0 (B=%d)", B);
   if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0)
     return fail(ATTN_ERR_SHAPE, "need Hq >= 1, Hkv >= 1 and Hq %% Hkv == 0 (Hq=%d Hkv=%d)",
@@ -236,7 +272,15 @@ int run_decode(const void* q, const void* k_cache, const void* v_cache,
   const size_t need = attn::decode_workspace_bytes(B, Hkv, Hq / Hkv, D, workers);
   void* ws = workspace;
   std::unique_lock<std::mutex> ws_lock(g_ws_mutex, std::defer_lock);
-  if (ws) {
+  if (use_scratch) {
+    // the fixed device array: nothing is allocated; a problem that does not fit is refused
+    if (need > kScratchBytes)
+      return fail(ATTN_ERR_WORKSPACE, "this decode needs %zu bytes of partial results, more than "
+                  "the %zu bytes of fixed scratch of attn_decode_paged_noalloc (fewer worker "
+                  "waves, a smaller batch, or attn_decode_paged_ex with a caller workspace)",
+                  need, kScratchBytes);
+    if (int rc = scratch_address(&ws)) return rc;
+  } else if (ws) {
     if (workspace_bytes < need)
       return fail(ATTN_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed",
                   workspace_bytes, need);
@@ -376,6 +420,18 @@ int attn_decode_paged_ex(const void* q, const void* k_cache, const void* v_cache
                     workspace_bytes, stream);
 }
 
+int attn_decode_paged_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_table, const int32_t* ctx_lens, void* o,
+                              float* lse, int B, int Hq, int Hkv, int D, int block_size,
+                              float scale, int table_stride, int num_blocks, int num_workers,
+                              void* stream) {
+  return run_decode(q, k_cache, v_cache, block_table, ctx_lens, o, lse, B, Hq, Hkv, D,
+                    block_size, scale, table_stride, num_blocks, num_workers, nullptr, 0, stream,
+                    /*use_scratch=*/true);
+}
+
+size_t attn_decode_noalloc_max_bytes(void) { return kScratchBytes; }
+
 size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int D, int num_workers) {
   if (B < 0 || B > 65535 || Hq < 1 || Hkv < 1 || Hkv > 65535 || Hq % Hkv != 0 ||
       Hq / Hkv > 16 || (D != 64 && D != 128) || num_workers < 0 || num_workers > kMaxWorkers)
@@ -420,6 +476,6 @@ void attn_release_workspace(void) {
   if (have_cur) (void)hipSetDevice(cur);
 }
 
-int attn_abi_version(void) { return 6; }
+int attn_abi_version(void) { return 7; }
 
 }  // extern "C"

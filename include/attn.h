@@ -134,6 +134,25 @@ int attn_decode_paged_ex(const void* q, const void* k_cache, const void* v_cache
                          float scale, int table_stride, int num_blocks, int num_workers,
                          void* workspace, size_t workspace_bytes, void* stream);
 
+/* attn_decode_paged_ex for callers that cannot allocate device memory (code under graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same kernels and result,
+ * but the partial results live in a fixed device array of attn_decode_noalloc_max_bytes()
+ * bytes (8 MiB) inside the library, one per device, held until the process ends. The call
+ * allocates and frees nothing. Arguments as for attn_decode_paged_ex, without a workspace.
+ * A problem whose attn_decode_workspace_bytes(B, Hq, Hkv, D, num_workers) exceeds that size
+ * returns ATTN_ERR_WORKSPACE (e.g. B = 64, Hq = 32, Hkv = 8, D = 128 at the default 768
+ * workers needs 2.7 MB). Nothing in the array needs clearing between calls. Every call on a
+ * device shares that device's array: calls that overlap in time on one device (two streams,
+ * or two host threads) race on it and give wrong results; serialise them. */
+int attn_decode_paged_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_table, const int32_t* ctx_lens, void* o,
+                              float* lse, int B, int Hq, int Hkv, int D, int block_size,
+                              float scale, int table_stride, int num_blocks, int num_workers,
+                              void* stream);
+
+/* Size in bytes of the fixed array attn_decode_paged_noalloc uses. */
+size_t attn_decode_noalloc_max_bytes(void);
+
 /* Bytes of workspace the decode needs (num_workers 0 = the default):
  * (W + B * Hkv) partial results of (Hq / Hkv) heads x (D + 2) floats, 16-byte padded, plus
  * 2 int32 per (sequence, KV head). 0 for invalid arguments. */
@@ -203,7 +222,7 @@ const char* attn_last_error(void);
  * that hold them). No call may be running or enqueued-and-unfinished when it is called. */
 void attn_release_workspace(void);
 
-/* ABI version of this header: 6. */
+/* ABI version of this header: 7. */
 int attn_abi_version(void);
 
 #ifdef __cplusplus

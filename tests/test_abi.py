@@ -42,7 +42,7 @@ def test_status_strings_and_version():
     for code in range(9):
         assert A.attn_status_string(code) not in ("", "unknown status")
     assert A.attn_status_string(99) == "unknown status"
-    assert A.attn_abi_version() == 6
+    assert A.attn_abi_version() == 7
 
 
 def fwd(*, q=P, k=P, v=P, o=P, lse=0, B=1, Hq=32, Hkv=8, Sq=128, Sk=128, D=128, causal=1,
@@ -135,6 +135,31 @@ def test_decode_workspace_size():
     # one byte less than the reported size is refused before anything is launched
     need = A.attn_decode_workspace_bytes(64, 32, 8, 128, 4)
     assert dec(workers=4, ws_bytes=need - 1) == WS
+
+
+def noalloc(*, q=P, kc=P, vc=P, table=P, ctx=P, o=P, lse=0, B=64, Hq=32, Hkv=8, D=128, bs=16,
+            scale=0.08, stride=256, nblocks=0, workers=768):
+    return A.load_library().attn_decode_paged_noalloc(q, kc, vc, table, ctx, o, lse, B, Hq, Hkv,
+                                                      D, bs, scale, stride, nblocks, workers,
+                                                      None)
+
+
+def test_decode_noalloc_checks_before_anything_else():
+    """The allocation-free decode validates like the _ex entry point and refuses a problem
+    whose partial results do not fit its fixed array, all before touching the device."""
+    cap = A.attn_decode_noalloc_max_bytes()
+    assert cap == 8 << 20
+    assert noalloc(q=0) == NULL
+    assert noalloc(bs=32) == UNSUP
+    assert noalloc(kc=P + 2) == ALIGN
+    assert noalloc(scale=NAN) == SCALE
+    assert noalloc(Hq=33) == SHAPE
+    assert noalloc(B=0) == OK
+    # the largest batch at 768 workers that fits, and the next one that does not
+    fits = max(b for b in range(1, 4096) if ws_bytes(b, 32, 8, 128, 768) <= cap)
+    assert noalloc(B=fits + 1) == WS
+    assert "fixed scratch" in A.attn_last_error()
+    assert noalloc(B=1, workers=65536) == WS     # too many worker slots
 
 
 def test_binding_rejects_cpu_tensors():

@@ -16,7 +16,8 @@ import os
 
 __all__ = [
     "AttnError", "library_path", "load_library",
-    "attn_fwd", "attn_fwd_f32", "attn_fwd_ex", "attn_fwd_workspace_bytes", "attn_decode_paged",
+    "attn_fwd", "attn_fwd_f32", "attn_fwd_ex", "attn_fwd_workspace_bytes", "attn_fwd_force_mapping",
+    "FWD_MAPPINGS", "attn_decode_paged",
     "attn_decode_paged_ex", "attn_decode_paged_noalloc", "attn_decode_noalloc_max_bytes",
     "attn_decode_workspace_bytes", "attn_decode_default_workers", "attn_status_string",
     "attn_last_error", "attn_release_workspace", "attn_abi_version", "attn_add_rms_norm",
@@ -33,6 +34,7 @@ _SIGNATURES = {
     "attn_fwd_f32": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P]),
     "attn_fwd_ex": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P, _Z, _P]),
     "attn_fwd_workspace_bytes": (_Z, [_I, _I, _I, _I, _I, _I, _I]),
+    "attn_fwd_force_mapping": (_I, [_I]),
     "attn_decode_paged": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P]),
     "attn_decode_paged_ex": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I,
                                   _I, _P, _Z, _P]),
@@ -212,6 +214,19 @@ def attn_fwd_ex(*args, **kw):
 
 def attn_fwd_workspace_bytes(B, Hq, Hkv, Sq, Sk, D, causal) -> int:
     return load_library().attn_fwd_workspace_bytes(B, Hq, Hkv, Sq, Sk, D, 1 if causal else 0)
+
+
+FWD_MAPPINGS = {"tile": 0, "pair": 1, "wide": 2}
+
+
+def attn_fwd_force_mapping(mapping) -> int:
+    """Force the bf16 forward's work mapping ("tile", "pair", "wide" or its number; None or -1 =
+    chosen per problem) for measurement and testing; returns the previous setting."""
+    if mapping is None:
+        mapping = -1
+    elif isinstance(mapping, str):
+        mapping = FWD_MAPPINGS[mapping]
+    return load_library().attn_fwd_force_mapping(int(mapping))
 
 
 def attn_fwd_f32(q, k, v, causal=False, scale=None, out=None, lse=None, want_lse=True,

@@ -34,6 +34,9 @@ FILE_FLAGS = {
     # the decode kernel needs few registers; with the accumulators in ordinary VGPRs the
     # per-block rescale runs on them directly instead of copying through AGPRs
     "attn_decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    # the wide forward: score accumulators must be ordinary VGPRs (the softmax reads them);
+    # the register allocator then keeps the K/Q operands in the accumulation registers
+    "attn_fwd_wide.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form=1"],
 }
 
 

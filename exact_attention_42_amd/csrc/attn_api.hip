@@ -13,6 +13,7 @@
 #include <utility>
 #include <vector>
 #include <algorithm>
+#include <atomic>
 
 #include "attn.h"
 #include "kernels.hpp"
@@ -133,17 +134,21 @@ int default_workers() {
   return w > kMaxWorkers ? kMaxWorkers : w;
 }
 
-// Forced work mapping of the bf16 forward: ATTN_FWD_MAPPING = "tile" or "pair" (for
-// measurement); unset or anything else = chosen per problem.
+// Forced work mapping of the bf16 forward (-1 = chosen per problem). Starts from
+// ATTN_FWD_MAPPING = "tile", "pair" or "wide" when set; attn_fwd_force_mapping changes it.
+std::atomic<int> g_forced_mapping{-2};   // -2: not read from the environment yet
+
 int forced_fwd_mapping() {
-  static const int m = [] {
-    const char* s = std::getenv("ATTN_FWD_MAPPING");
-    if (!s) return -1;
-    if (std::strcmp(s, "tile") == 0) return (int)attn::kMapTile;
-    if (std::strcmp(s, "pair") == 0) return (int)attn::kMapPair;
-    return -1;
-  }();
-  return m;
+  int m = g_forced_mapping.load(std::memory_order_relaxed);
+  if (m != -2) return m;
+  const char* s = std::getenv("ATTN_FWD_MAPPING");
+  m = -1;
+  if (s && std::strcmp(s, "tile") == 0) m = (int)attn::kMapTile;
+  if (s && std::strcmp(s, "pair") == 0) m = (int)attn::kMapPair;
+  if (s && std::strcmp(s, "wide") == 0) m = (int)attn::kMapWide;
+  int expected = -2;
+  g_forced_mapping.compare_exchange_strong(expected, m);
+  return g_forced_mapping.load(std::memory_order_relaxed);
 }
 
 // The library workspace of (current device, stream), at least need bytes. The caller must hold
@@ -216,10 +221,10 @@ int run_fwd(bool f32, const void* q, const void* k, const void* v, void* o, floa
     return fail(ATTN_ERR_SHAPE, "Sk=%d too long for D=%d: Sk*D*2 must stay below 2^31", Sk, D);
   if (empty) return ok();
   attn::FwdProblem p{q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, causal ? 1 : 0, scale, 1, nullptr,
-                     forced_fwd_mapping()};
+                     forced_fwd_mapping(), device_cus()};
   std::unique_lock<std::mutex> ws_lock(g_ws_mutex, std::defer_lock);
-  if (!f32) {
-    p.nsplit = attn::fwd_bf16_splits(p, device_cus());
+  if (!f32 && p.mapping < 0) {
+    p.nsplit = attn::fwd_bf16_splits(p, p.cus);
     if (p.nsplit > 1) {
       const size_t need = attn::fwd_bf16_workspace_bytes(p, p.nsplit);
       if (workspace) {
@@ -381,6 +386,13 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
                  stream);
 }
 
+int attn_fwd_force_mapping(int mapping) {
+  const int prev = forced_fwd_mapping();
+  const int m = (mapping >= (int)attn::kMapTile && mapping <= (int)attn::kMapWide) ? mapping : -1;
+  g_forced_mapping.store(m, std::memory_order_relaxed);
+  return prev;
+}
+
 int attn_fwd_f32(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                  int Hq, int Hkv, int Sq, int Sk, int D, int causal, float scale, void* stream) {
   return run_fwd(true, q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, causal, scale, nullptr, 0,
@@ -399,7 +411,8 @@ size_t attn_fwd_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk, int D, i
       (long long)B * Hq > 0x7fffffffLL || Sq > (1 << 30) || Sk > (1 << 30))
     return 0;
   attn::FwdProblem p{nullptr, nullptr, nullptr, nullptr, nullptr, B, Hq, Hkv, Sq, Sk, D,
-                     causal ? 1 : 0, 1.0f, 1, nullptr, -1};
+                     causal ? 1 : 0, 1.0f, 1, nullptr, forced_fwd_mapping(), device_cus()};
+  if (p.mapping >= 0) return 0;
   return attn::fwd_bf16_workspace_bytes(p, attn::fwd_bf16_splits(p, device_cus()));
 }
 
@@ -476,6 +489,6 @@ void attn_release_workspace(void) {
   if (have_cur) (void)hipSetDevice(cur);
 }
 
-int attn_abi_version(void) { return 7; }
+int attn_abi_version(void) { return 8; }
 
 }  // extern "C"

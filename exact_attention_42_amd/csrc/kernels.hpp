@@ -20,10 +20,11 @@ struct FwdProblem {
   int nsplit;        // bf16: key-range splits per query tile (<= 1: none)
   void* workspace;   // bf16 with nsplit > 1: fwd_bf16_workspace_bytes(p, nsplit) bytes
   int mapping;       // bf16 without splits: FwdMapping, or -1 to choose by the problem
+  int cus = 256;     // compute units of the device (for the choice of mapping)
 };
 
 // Work mappings of the bf16 forward without key-range splits.
-enum FwdMapping { kMapTile = 0, kMapPair = 1 };
+enum FwdMapping { kMapTile = 0, kMapPair = 1, kMapWide = 2 };
 
 // The mapping the bf16 forward uses for p (without key-range splits) when none is forced.
 int fwd_bf16_mapping(const FwdProblem& p, int cus);
@@ -34,6 +35,9 @@ int fwd_bf16_splits(const FwdProblem& p, int cus);
 size_t fwd_bf16_workspace_bytes(const FwdProblem& p, int nsplit);
 // bf16 Q/K/V/O, fp32 LSE; MFMA kernel. D in {64, 128}.
 hipError_t launch_fwd_bf16(const FwdProblem& p, hipStream_t stream);
+// The wide mapping of the bf16 forward (one wave per SIMD, 256 query rows per workgroup);
+// D = 128, no key-range splits.
+hipError_t launch_fwd_bf16_wide(const FwdProblem& p, hipStream_t stream);
 // fp32 Q/K/V/O, fp32 LSE; vector-ALU kernel. D in {64, 128}.
 hipError_t launch_fwd_f32(const FwdProblem& p, hipStream_t stream);
 

@@ -89,6 +89,18 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse
  * (0 when it runs without key-range splits or the arguments are invalid). */
 size_t attn_fwd_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk, int D, int causal);
 
+/* Work mapping of the bf16 forward, for measurement and testing:
+ *   0 "tile": one 4-wave workgroup per 128-row query tile;
+ *   1 "pair": causal light/heavy tile pairs in one 8-wave workgroup (causal calls only; others
+ *      run the tile kernel);
+ *   2 "wide": one wave per SIMD, 64 rows per wave, 256-row workgroups (D = 128 only; other D
+ *      run the tile kernel);
+ *   anything else: chosen per problem (the default). ATTN_FWD_MAPPING = tile / pair / wide sets
+ *   the initial value.
+ * A forced mapping never splits key ranges. Process-wide; returns the previous setting
+ * (-1 = chosen per problem). Every mapping computes the same result up to rounding order. */
+int attn_fwd_force_mapping(int mapping);
+
 /* The same computation with float32 q, k, v, o (full-precision path; no workspace). */
 int attn_fwd_f32(const void* q, const void* k, const void* v, void* o, float* lse,
                  int B, int Hq, int Hkv, int Sq, int Sk, int D,
@@ -222,7 +234,7 @@ const char* attn_last_error(void);
  * that hold them). No call may be running or enqueued-and-unfinished when it is called. */
 void attn_release_workspace(void);
 
-/* ABI version of this header: 7. */
+/* ABI version of this header: 8. */
 int attn_abi_version(void);
 
 #ifdef __cplusplus

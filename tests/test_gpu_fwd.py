@@ -362,3 +362,116 @@ def test_key_split_and_whole_paths(B, Hq, Hkv, Sq, Sk, causal, dev):
     O, L = oracle.attention(q, k, v, causal=causal, scale=scale)
     check_bf16(o, O)
     check_lse(lse, L)
+
+
+# ---- the wide kernel (one wave per SIMD, 256-row workgroups) ----
+
+@pytest.fixture
+def forced_wide():
+    prev = A.attn_fwd_force_mapping("wide")
+    yield
+    A.attn_fwd_force_mapping(prev)
+
+
+WIDE_SMALL = [
+    # B, Hq, Hkv, Sq, Sk, causal: ragged query and key tails, Sq above and below Sk, GQA, one
+    # query, one key, shapes whose waves end 1-3 tiles before their workgroup's last tile
+    (1, 1, 1, 256, 256, True), (1, 1, 1, 256, 256, False), (1, 2, 1, 300, 300, True),
+    (2, 4, 2, 200, 200, False), (1, 2, 1, 100, 300, True), (1, 2, 1, 300, 100, True),
+    (1, 2, 2, 1, 777, True), (1, 2, 2, 70, 1, False), (1, 4, 4, 1000, 1000, True),
+    (2, 2, 1, 640, 700, True), (1, 2, 1, 2048, 2048, True), (1, 2, 2, 513, 2000, False),
+    (1, 3, 1, 1200, 900, True), (1, 2, 2, 2100, 2100, True), (1, 8, 1, 257, 1025, True),
+    (3, 2, 2, 511, 65, True), (1, 1, 1, 64, 64, True), (1, 2, 1, 320, 3000, False),
+]
+
+
+@pytest.mark.parametrize("shape", WIDE_SMALL, ids=lambda s: "x".join(map(str, s)))
+def test_fwd_wide_small(shape, dev, forced_wide):
+    B, Hq, Hkv, Sq, Sk, causal = shape
+    q, k, v = W.fwd_inputs(B, Hq, Hkv, Sq, Sk, 128, seed=1234 + Sq + Sk)
+    scale = np.float32(1 / np.sqrt(128))
+    o, lse = run_bf16(q, k, v, causal, scale, dev)
+    O, L = oracle.attention(q, k, v, causal=causal, scale=scale)
+    check_bf16(o, O, what=f"{shape} O")
+    check_lse(lse, L, what=f"{shape} LSE")
+
+
+def random_wide_shape(seed):
+    """Seeded shapes for the wide kernel: 1-3 batch entries, GQA 1:1 to 8:1, 1-1800 queries
+    and 1-3000 keys (both signs of the causal offset), causal or not."""
+    rng = np.random.default_rng(4200 + seed)
+    B = int(rng.integers(1, 4))
+    Hkv = int(rng.integers(1, 3))
+    Hq = Hkv * int(rng.choice([1, 2, 4, 8]))
+    Sq = int(rng.integers(1, 1800))
+    Sk = int(rng.integers(1, 3000))
+    causal = bool(rng.integers(0, 2))
+    return B, Hq, Hkv, Sq, Sk, causal
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_fwd_wide_random_shapes(seed, dev, forced_wide):
+    B, Hq, Hkv, Sq, Sk, causal = random_wide_shape(seed)
+    q, k, v = W.fwd_inputs(B, Hq, Hkv, Sq, Sk, 128, seed=5200 + seed)
+    scale = np.float32(1 / np.sqrt(128))
+    o, lse = run_bf16(q, k, v, causal, scale, dev)
+    O, L = oracle.attention(q, k, v, causal=causal, scale=scale)
+    what = f"B={B} Hq={Hq} Hkv={Hkv} Sq={Sq} Sk={Sk} causal={causal}"
+    check_bf16(o, O, what=what + " O")
+    check_lse(lse, L, what=what + " LSE")
+
+
+def test_fwd_wide_is_deterministic(dev, forced_wide):
+    """Repeated launches give identical bits (the four LDS stages and the spread loads leave no
+    race)."""
+    q, k, v = W.fwd_inputs(2, 8, 2, 1100, 1100, 128, seed=19)
+    qg, kg, vg = (_gpu(x, dev, torch.bfloat16) for x in (q, k, v))
+    ref, ref_l = A.attn_fwd(qg, kg, vg, causal=True)
+    for _ in range(30):
+        o, l = A.attn_fwd(qg, kg, vg, causal=True)
+        assert torch.equal(o, ref) and torch.equal(l, ref_l)
+
+
+@pytest.mark.parametrize("Sq", [768, 769])
+def test_wide_default_switch(Sq, dev):
+    """D=128 problems with at least four 256-row work items per CU run the wide kernel by
+    default: 4 x 64 heads x ceil(769/256) = 1024 items does (its output equals the forced wide
+    kernel's bit for bit), 768 rows (768 items) does not; both sides against the oracle on
+    sampled rows."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    if cus != 256:
+        pytest.skip(f"the switch point is sized for 256 CUs (this device has {cus})")
+    B, Hq, Hkv = 4, 64, 8
+    q, k, v = W.fwd_inputs(B, Hq, Hkv, Sq, Sq, 128, seed=Sq)
+    qg, kg, vg = (_gpu(x, dev, torch.bfloat16) for x in (q, k, v))
+    scale = float(np.float32(1 / np.sqrt(128)))
+    o, lse = A.attn_fwd(qg, kg, vg, causal=True, scale=scale)
+    prev = A.attn_fwd_force_mapping("wide")
+    try:
+        ow, lw = A.attn_fwd(qg, kg, vg, causal=True, scale=scale)
+    finally:
+        A.attn_fwd_force_mapping(prev)
+    torch.cuda.synchronize()
+    same = torch.equal(o, ow) and torch.equal(lse, lw)
+    assert same == (Sq == 769)
+    rows = W.sample_rows(B, Hq, Sq, 128, seed=Sq, must=[0, 255, 256, 511, 512, Sq - 1])
+    O, L = oracle.attention_rows(q, k, v, rows, causal=True, scale=np.float32(scale))
+    idx = tuple(np.array(rows).T)
+    check_bf16(to_np(o)[idx], O, what=f"Sq={Sq} sampled O")
+    check_lse(to_np(lse)[idx], L, what=f"Sq={Sq} sampled LSE")
+
+
+def test_forced_mapping_falls_back(dev):
+    """A forced wide mapping with D=64, and a forced pair mapping on a non-causal call, run the
+    tile kernel (both still match the oracle)."""
+    for mapping, D, causal in (("wide", 64, True), ("pair", 128, False)):
+        prev = A.attn_fwd_force_mapping(mapping)
+        try:
+            q, k, v = W.fwd_inputs(1, 4, 2, 300, 300, D, seed=D)
+            scale = np.float32(1 / np.sqrt(D))
+            o, lse = run_bf16(q, k, v, causal, scale, dev)
+        finally:
+            A.attn_fwd_force_mapping(prev)
+        O, L = oracle.attention(q, k, v, causal=causal, scale=scale)
+        check_bf16(o, O)
+        check_lse(lse, L)

@@ -31,10 +31,11 @@
 // every pending P^T valid without rescaling it.
 //
 // K/V staging: 64-key tiles in 4 LDS stages (32 KiB each: K then V), filled by the four waves'
-// direct-to-LDS buffer loads. A wave's 8 loads of a tile go out two at a time at boundaries
-// between its stretches (a burst of them would stall in-order issue while the memory pipeline
-// drains), starting after the workgroup barrier in the middle of tile T - 3's second block,
-// into the stage tile T - 4 used; that barrier also guarantees tile T - 2 has landed.
+// direct-to-LDS buffer loads. A wave's 8 loads of a tile go out one at a time between its
+// matrix-core instructions (the four waves reach a load together, and a few of them at once
+// already stall in-order issue while the address unit works through them), starting after the
+// workgroup barrier in the middle of tile T - 3's second block, into the stage tile T - 4 used;
+// that barrier also guarantees tile T - 2 has landed.
 // Each stage is a separate LDS object so the compiler can tell the in-flight loads into one
 // stage from reads of another.
 #include <type_traits>
@@ -56,7 +57,7 @@ constexpr int kStages = 4;
 // s_waitcnt immediates, gfx9 encoding (vmcnt in bits 3:0 and 15:14, expcnt and lgkmcnt free)
 constexpr int kWaitVm0 = 0x0F70;
 constexpr int kWaitVm8 = 0x0F78;
-constexpr int kWaitVm12 = 0x0F7C;
+constexpr int kWaitVm11 = 0x0F7B;
 
 template <int D>
 struct WideWave {
@@ -84,22 +85,22 @@ struct WidePipe {
   u32x4 p0[2][2];        // group 0 P^T of the previous block (product with V pending)
 };
 
-template <int D>
+template <int D, int FIRST = 0, int LAST = Geo<D, 4>::KS>
 __device__ __forceinline__ void read_k(const WideWave<D>& w, const char* kblk,
                                        u32x4 (&kf)[Geo<D, 4>::KS]) {
 #pragma unroll
-  for (int kk = 0; kk < Geo<D, 4>::KS; ++kk)
+  for (int kk = FIRST; kk < LAST; ++kk)
     kf[kk] = *reinterpret_cast<const u32x4*>(kblk + w.koff[kk]);
 }
 
 // V^T fragments of a 32-key block, index 2*db + t: keys 16t + 4h + {0..3} in slots (h, 0..3)
 // and 16t + 8 + 4h + {0..3} in slots (h, 4..7), matching the P^T slots.
-template <int D>
+template <int D, int FIRST = 0, int LAST = 2 * Geo<D, 4>::DB>
 __device__ __forceinline__ void read_v(const WideWave<D>& w, const char* vblk,
                                        u32x4 (&vf)[2 * Geo<D, 4>::DB]) {
   using G = Geo<D, 4>;
 #pragma unroll
-  for (int i = 0; i < 2 * G::DB; ++i) {
+  for (int i = FIRST; i < LAST; ++i) {
     const char* vp = vblk + w.voff[i >> 1] + 16 * (i & 1) * G::kRow;
     const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vp));
     const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vp + 8 * G::kRow));
@@ -236,8 +237,6 @@ __device__ __forceinline__ void wide_iter(WideWave<D>& w, WidePipe<D>& p, const 
   static_assert(KS == 8 && NV == 8, "D = 128");
   constexpr int IN = EVEN ? 1 : 0, OUT = 1 - IN;   // pending-state slots read and written
   stretch_end();
-  hook(0);
-  stretch_end();
 
   // ---- 1a ----
   u32x4 vf[NV];
@@ -249,6 +248,7 @@ __device__ __forceinline__ void wide_iter(WideWave<D>& w, WidePipe<D>& p, const 
   for (int kk = 0; kk < KS; ++kk) {
     s0 = mfma32x32x16(p.kf[kk], w.qf[0][kk], s0);
     if (kk & 1) p1[0][kk >> 1] = exp_pair(p.s1[IN], 0, kk >> 1, c, p.mu1[IN], la, lb);
+    hook(0, kk);
   }
   stretch_pattern<2, 1, 3>();
   pin(s0);
@@ -257,8 +257,7 @@ __device__ __forceinline__ void wide_iter(WideWave<D>& w, WidePipe<D>& p, const 
   pin(lb);
   stretch_end();
 
-  // ---- 1b ---- (a load and the mask (rare) between the stretches)
-  hook(1);
+  // ---- 1b ---- (the mask, rare, between the stretches)
   if (mask) mask_block(s0, w.lim[0], k0, h);
   stretch_end();
   f32x16 s1 = f32x16{};
@@ -275,6 +274,7 @@ __device__ __forceinline__ void wide_iter(WideWave<D>& w, WidePipe<D>& p, const 
     if (kk == 5) row_max_c(r0);
     if (kk == 6) p1[1][3] = exp_pair(p.s1[IN], 1, 3, c, p.mu1[IN], la, lb);
     if (kk == 7) any0 = must_move(r0.mx, w.thr[0], move0);
+    hook(1, kk);
   }
   w.l[1] += la + lb;
   stretch_pattern<0, 1, 5>();
@@ -292,8 +292,6 @@ __device__ __forceinline__ void wide_iter(WideWave<D>& w, WidePipe<D>& p, const 
   mid();
   asm volatile("" ::: "memory");
   stretch_end();
-  hook(2);
-  stretch_end();
 
   // ---- 2a ----
   u32x4 (&p0n)[2] = p.p0[OUT];
@@ -303,6 +301,7 @@ __device__ __forceinline__ void wide_iter(WideWave<D>& w, WidePipe<D>& p, const 
   for (int i = 0; i < NV; ++i) {
     w.o[0][i >> 1] = mfma32x32x16(vf[i], p.p0[IN][i & 1], w.o[0][i >> 1]);
     if (i & 1) p0n[0][i >> 1] = exp_pair(s0, 0, i >> 1, c, mu0, la, lb);
+    hook(2, i);
   }
   stretch_pattern<0, 1, 3>();
   pin(p0n[0]);
@@ -310,8 +309,7 @@ __device__ __forceinline__ void wide_iter(WideWave<D>& w, WidePipe<D>& p, const 
   pin(lb);
   stretch_end();
 
-  // ---- 2b ---- (a load and the mask (rare) between the stretches)
-  hook(3);
+  // ---- 2b ---- (the mask, rare, between the stretches)
   if (mask) mask_block(s1, w.lim[1], k0, h);
   stretch_end();
   // (the current K fragments were last used in 1b: the next block's go into the same registers)
@@ -329,6 +327,7 @@ __device__ __forceinline__ void wide_iter(WideWave<D>& w, WidePipe<D>& p, const 
     if (i == 5) row_max_c(r1);
     if (i == 6) p0n[1][3] = exp_pair(s0, 1, 3, c, mu0, la, lb);
     if (i == 7) any1 = must_move(r1.mx, w.thr[1], move1);
+    hook(3, i);
   }
   w.l[0] += la + lb;
   stretch_pattern_early_ds<4, 1, 5>();
@@ -349,8 +348,6 @@ __device__ __forceinline__ void wide_iter(WideWave<D>& w, WidePipe<D>& p, const 
   }
   p.s1[OUT] = s1;
   p.mu1[OUT] = w.m[1];
-  stretch_end();
-  hook(4);
   stretch_end();
 }
 
@@ -497,23 +494,21 @@ __device__ __forceinline__ void fwd_wide_body(const FwdArgs& a) {
   }
   TileDma<D, 4> dma;
   dma.init(wave, lane, kbase, vbase, a.Sk);
-  // Loads: tile X's 8 loads per wave go out two at a time at stretch boundaries of iterations
-  // 2X - 5 (after the barrier) and 2X - 4, into the stage of tile X - 4, which no wave reads
-  // after barrier X - 3. Tiles 0 and 1 and the first four loads of tile 2 are issued here; then
-  // wait for tile 0 (and the Q fragments, loaded earlier).
+  // Loads: a wave's 8 loads of tile X go out one at a time between the matrix-core instructions
+  // of iterations 2X - 5 (after its barrier: loads 0..2) and 2X - 4 (loads 3..7), into the stage
+  // of tile X - 4, which no wave reads after barrier X - 3. Every load is issued, so the count of
+  // loads in flight after tile T + 1's is always 8 at barrier T: a tile past the workgroup's
+  // last loads, instead, the tile its stage already holds (X - 4, the same bytes), or for X < 4
+  // tile X itself into a stage no tile uses. Tiles 0 and 1 and the first three loads of tile 2
+  // are issued here; then wait for tile 0 (and the Q fragments, loaded earlier).
   constexpr int kParts = 2 * G::kIPW;      // loads per wave and tile
   static_assert(kParts == 8, "D = 128: 4 K and 4 V loads per wave and tile");
 #pragma unroll
   for (int t = 0; t < 3; ++t) {
-    if (t < nt) {
 #pragma unroll
-      for (int j = 0; j < (t < 2 ? kParts : 4); ++j)
-        dma.issue_part_unclamped(KS[t], VS[t], t * kBN, j);
-    }
+    for (int j = 0; j < (t < 2 ? kParts : 3); ++j) dma.issue_part_unclamped(KS[t], VS[t], t * kBN, j);
   }
-  if (nt > 2) __builtin_amdgcn_s_waitcnt(kWaitVm12);
-  else if (nt == 2) __builtin_amdgcn_s_waitcnt(kWaitVm8);
-  else __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  __builtin_amdgcn_s_waitcnt(kWaitVm11);
   __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
@@ -532,11 +527,12 @@ __device__ __forceinline__ void fwd_wide_body(const FwdArgs& a) {
   auto mid_for = [&](int T) {
     return [&, T]() {
       if (T + 1 >= nt) return;
-      if (T + 2 < nt) __builtin_amdgcn_s_waitcnt(kWaitVm8);
-      else __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      __builtin_amdgcn_s_waitcnt(kWaitVm8);
       __builtin_amdgcn_s_barrier();
     };
   };
+  // the tile whose bytes a load for tile X fetches (see above)
+  auto load_tile = [&](int X) { return X < nt ? X : (X >= 4 ? X - 4 : X); };
   auto nothing = []() {};
 
   // one 64-key tile (blocks 2T and 2T + 1) with its stages fixed at compile time
@@ -551,38 +547,36 @@ __device__ __forceinline__ void fwd_wide_body(const FwdArgs& a) {
     char* const k3 = KS[(ST + 3) % kStages];               // tile T + 3 (loads 0..2 now)
     char* const v3 = VS[(ST + 3) % kStages];
     const int k0 = T * kBN;
-    const bool more2 = T + 2 < nt, more3 = T + 3 < nt;
-    // loads 4..7 of tile T + 2 at the first two boundaries of block 2T, loads 0..3 of tile T + 3
-    // at the last two of block 2T + 1 (after its barrier)
-    auto hook0 = [&](int b) {
-      if (b < 2 && more2) {
-        dma.issue_part_unclamped(k2, v2, (T + 2) * kBN, 4 + 2 * b);
-        dma.issue_part_unclamped(k2, v2, (T + 2) * kBN, 5 + 2 * b);
-      }
+    const int kt2 = load_tile(T + 2) * kBN, kt3 = load_tile(T + 3) * kBN;
+    // loads 3..7 of tile T + 2 spread over block 2T (stretches 1a, 1a, 2a, 2a, 2b), loads 0..2
+    // of tile T + 3 over the stretches of block 2T + 1 after its barrier (2a, 2b, 2b)
+    auto hook0 = [&](int st, int slot) {
+      if (st == 0 && slot == 1) dma.issue_part_unclamped(k2, v2, kt2, 3);
+      if (st == 0 && slot == 5) dma.issue_part_unclamped(k2, v2, kt2, 4);
+      if (st == 2 && slot == 1) dma.issue_part_unclamped(k2, v2, kt2, 5);
+      if (st == 2 && slot == 5) dma.issue_part_unclamped(k2, v2, kt2, 6);
+      if (st == 3 && slot == 3) dma.issue_part_unclamped(k2, v2, kt2, 7);
     };
-    auto hook1 = [&](int b) {
-      if (b >= 3 && more3) {
-        dma.issue_part_unclamped(k3, v3, (T + 3) * kBN, 2 * (b - 3));
-        dma.issue_part_unclamped(k3, v3, (T + 3) * kBN, 2 * (b - 3) + 1);
-      }
+    auto hook1 = [&](int st, int slot) {
+      if (st == 2 && slot == 3) dma.issue_part_unclamped(k3, v3, kt3, 0);
+      if (st == 3 && slot == 1) dma.issue_part_unclamped(k3, v3, kt3, 1);
+      if (st == 3 && slot == 5) dma.issue_part_unclamped(k3, v3, kt3, 2);
     };
     auto mid = mid_for(T);
     const int i = 2 * T;
     if (i < nblk) {
       wide_iter<D, true>(w, p, vp + 32 * G::kRow, kc + 32 * G::kRow, k0, i >= nunm, h, c,
                          a_inv_c, nothing, hook0);
-    } else if (more2) {
+    } else {
 #pragma unroll
-      for (int j = 4; j < kParts; ++j) dma.issue_part_unclamped(k2, v2, (T + 2) * kBN, j);
+      for (int j = 3; j < kParts; ++j) dma.issue_part_unclamped(k2, v2, kt2, j);
     }
     if (i + 1 < nblk) {
       wide_iter<D, false>(w, p, vc, kn, k0 + 32, i + 1 >= nunm, h, c, a_inv_c, mid, hook1);
     } else {
       mid();
-      if (more3) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) dma.issue_part_unclamped(k3, v3, (T + 3) * kBN, j);
-      }
+      for (int j = 0; j < 3; ++j) dma.issue_part_unclamped(k3, v3, kt3, j);
     }
   };
 

@@ -609,7 +609,8 @@ def main():
     dbytes = decode_bytes(ctx_lens, DECODE)
     gbs = dbytes / (dec_ms * 1e-3) / 1e9
 
-    fwd_digest = source_digest("attn_fwd_bf16.hip", "cdna4.hpp")
+    fwd_digest = source_digest("attn_fwd_bf16.hip", "attn_fwd_wide.hip", "fwd_tiles.hpp",
+                               "cdna4.hpp")
     dec_digest = source_digest("attn_decode.hip", "cdna4.hpp", "attn_api.hip")
     clock_info = None
     if clock_mhz is not None:

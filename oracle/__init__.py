@@ -9,7 +9,7 @@ See ``oracle/direct.py`` (attention), ``oracle/rmsnorm.py`` (add_rms_norm) and
 ``oracle/rotary.py`` (rotary embedding + cache write) for what is computed and which passage
 each function follows.
 """
-from .direct import attention, attention_rows, decode_paged, gather_paged
+from .direct import attention, attention_rows, decode_paged, gather_paged, prefill_paged
 from .rmsnorm import add_rms_norm
 from .rotary import rope, rope_cache_write
 

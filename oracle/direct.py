@@ -168,3 +168,68 @@ def decode_paged(q, k_cache, v_cache, block_table, ctx_lens, block_size, scale=N
         O[b] = o[0, :, 0, :]
         L[b] = lse[0, :, 0]
     return O, L
+
+
+def prefill_paged(q, k_cache, v_cache, block_table, cu_seqlens_q, ctx_lens, block_size,
+                  causal=True, scale=None, num_blocks=0):
+    """Prefill of packed query tokens against a paged KV cache, in float64.
+
+    Prefill and decode are two schedules of one attention ("Kernel Fusion, Softmax, and
+    Attention", fifth paragraph); here the new tokens of each sequence attend to its cached
+    context, read through its block table ("Optimizing Large Language Model Inference ...",
+    §Paged Attention and Dynamic KV Cache Management).
+
+    q [T, Hq, D], sequence b owning rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1; caches
+    [num_blocks, Hkv, block_size, D]; block_table [B, *]; ctx_lens [B] keys per sequence, its
+    own query tokens being the last of them. Each sequence's context is gathered through the
+    table and its queries attend to it with the plain definition (``attention``), the causal
+    mask aligned to the bottom right (query i of n sits at position ctx - n + i). With
+    num_blocks > 0, the keys of a block whose table entry lies outside [0, num_blocks), or
+    that has no entry in the table's row, take no part. Returns O [T, Hq, D] and LSE [T, Hq];
+    rows that belong to no sequence stay O = 0, LSE = -inf.
+    """
+    q = np.asarray(q)
+    T, Hq, D = q.shape
+    Hkv = k_cache.shape[1]
+    O = np.zeros((T, Hq, v_cache.shape[3]), dtype=np.float64)
+    L = np.full((T, Hq), -np.inf, dtype=np.float64)
+    for b in range(len(ctx_lens)):
+        r0, r1 = int(cu_seqlens_q[b]), int(cu_seqlens_q[b + 1])
+        n, ctx = r1 - r0, int(ctx_lens[b])
+        if n <= 0:
+            continue
+        qb = np.transpose(q[r0:r1], (1, 0, 2))[None]           # [1, Hq, n, D]
+        if ctx <= 0:
+            continue                                            # no keys: O = 0, LSE = -inf
+        keep = np.ones(ctx, dtype=bool)
+        if num_blocks > 0:
+            t = np.arange(ctx)
+            lb = t // block_size
+            has = lb < block_table.shape[1]
+            phys = np.where(has, block_table[b, np.minimum(lb, block_table.shape[1] - 1)], -1)
+            keep = has & (phys >= 0) & (phys < num_blocks)
+        idx = np.nonzero(keep)[0]
+        if num_blocks > 0 and len(idx) < ctx:
+            # some keys take no part: attend each row over the kept keys it can see
+            t = np.arange(ctx)
+            safe = np.where(keep, t, 0)
+            Kb = np.transpose(k_cache[block_table[b, safe // block_size], :, safe % block_size, :],
+                              (1, 0, 2))
+            Vb = np.transpose(v_cache[block_table[b, safe // block_size], :, safe % block_size, :],
+                              (1, 0, 2))
+            for i in range(n):
+                pos = ctx - n + i
+                vis = keep & ((t <= pos) if causal else True)
+                sel = np.nonzero(vis)[0]
+                o, lse = attention(qb[:, :, i:i + 1, :], Kb[None][:, :, sel, :],
+                                   Vb[None][:, :, sel, :], causal=False, scale=scale)
+                O[r0 + i] = o[0, :, 0, :]
+                L[r0 + i] = lse[0, :, 0]
+            continue
+        Kb = gather_paged(k_cache, block_table, ctx, b, block_size)[None]
+        Vb = gather_paged(v_cache, block_table, ctx, b, block_size)[None]
+        o, lse = attention(qb, Kb, Vb, causal=causal, scale=scale)
+        O[r0:r1] = np.transpose(o[0], (1, 0, 2))
+        L[r0:r1] = lse[0].T
+    return O, L
+

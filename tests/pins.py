@@ -43,6 +43,10 @@ def _dec(*a, **kw):
     return OA.decode_paged(*a, **kw)
 
 
+def _prefill(*a, **kw):
+    return OA.prefill_paged(*a, **kw)
+
+
 def _norm(*a, **kw):
     return ON.add_rms_norm(*a, **kw)
 
@@ -436,6 +440,71 @@ def pin_decode_paged():
         _close(L3, L, 0.0, "poisoned tail LSE")
 
 
+# --- N3: prefill over a paged cache -----------------------------------------------------
+def pin_prefill_paged():
+    """A chunk of new tokens of each sequence, packed together with other sequences' chunks,
+    gets exactly the last rows of a full causal prefill over its whole sequence (the chunk's
+    tokens are the sequence's last positions); the last row of each chunk is the paged decode
+    of that token; without the mask every row is plain attention over the whole context;
+    slots past a context (NaN-poisoned) are never read; and with the pool size given, a block
+    whose table entry is outside the pool drops out as if its keys were not there."""
+    r = _rng(23)
+    Hq, Hkv, D, s = 4, 2, 8, 0.3
+    for bs in (4, 16):
+        lens = [5, bs, 2 * bs + 3, 37, 9, 6]       # keys of each sequence
+        qlens = [5, 1, bs + 2, 0, 3, 6]           # its new tokens: the last qlens positions
+        Ks = [r.standard_normal((Hkv, n, D)) for n in lens]
+        Vs = [r.standard_normal((Hkv, n, D)) for n in lens]
+        Qs = [r.standard_normal((Hq, n, D)) for n in lens]
+        kc, vc, table = _scatter_paged(Ks, Vs, bs, r)
+        for b, n in enumerate(lens):
+            last = table[b, (n - 1) // bs]
+            kc[last, :, (n - 1) % bs + 1:, :] = np.nan
+            vc[last, :, (n - 1) % bs + 1:, :] = np.nan
+        cu = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+        q = np.concatenate([np.transpose(Qs[b][:, n - m:, :], (1, 0, 2))
+                            for b, (n, m) in enumerate(zip(lens, qlens))])
+        ctx = np.array(lens, dtype=np.int32)
+        O, L = _prefill(q, kc, vc, table, cu, ctx, bs, causal=True, scale=s)
+        On, Ln = _prefill(q, kc, vc, table, cu, ctx, bs, causal=False, scale=s)
+        for b, (n, m) in enumerate(zip(lens, qlens)):
+            if m == 0:
+                continue
+            Of, Lf = _fwd(Qs[b][None], Ks[b][None], Vs[b][None], causal=True, scale=s)
+            _close(O[cu[b]:cu[b + 1]], np.transpose(Of[0][:, n - m:, :], (1, 0, 2)), 1e-13,
+                   f"chunk vs full prefill bs={bs} b={b}")
+            _close(L[cu[b]:cu[b + 1]], Lf[0][:, n - m:].T, 1e-13, f"chunk LSE bs={bs} b={b}")
+            Od, Ld = _dec(Qs[b][:, -1, :][None], kc, vc, table[b:b + 1], ctx[b:b + 1], bs,
+                          scale=s)
+            _close(O[cu[b + 1] - 1], Od[0], 1e-13, f"last chunk row vs decode bs={bs} b={b}")
+            _close(L[cu[b + 1] - 1], Ld[0], 1e-13, f"last chunk LSE vs decode bs={bs} b={b}")
+            Ou, Lu = _fwd(Qs[b][None][:, :, n - m:, :], Ks[b][None], Vs[b][None], causal=False,
+                          scale=s)
+            _close(On[cu[b]:cu[b + 1]], np.transpose(Ou[0], (1, 0, 2)), 1e-13,
+                   f"unmasked chunk bs={bs} b={b}")
+            _close(Ln[cu[b]:cu[b + 1]], Lu[0].T, 1e-13, f"unmasked LSE bs={bs} b={b}")
+        # a block outside the pool (sequence 3's third block) drops out when the pool is given
+        pool = kc.shape[0]
+        b, drop = 3, 2
+        table2 = table.copy()
+        table2[b, drop] = pool + 5
+        cu2 = np.array([0, 0, 0, 0, 4, 4, 4], dtype=np.int32)     # four new tokens of seq 3
+        n = lens[b]
+        q2 = np.transpose(Qs[b][:, n - 4:, :], (1, 0, 2))
+        keep = np.ones(n, dtype=bool)
+        keep[drop * bs:(drop + 1) * bs] = False
+        Ok, Lk = _prefill(q2, kc, vc, table2, cu2, ctx, bs, causal=False, scale=s,
+                          num_blocks=pool)
+        Oe, Le = _fwd(Qs[b][None][:, :, n - 4:, :], Ks[b][None][:, :, keep, :],
+                      Vs[b][None][:, :, keep, :], causal=False, scale=s)
+        _close(Ok, np.transpose(Oe[0], (1, 0, 2)), 1e-13, f"dropped block bs={bs}")
+        _close(Lk, Le[0].T, 1e-13, f"dropped block LSE bs={bs}")
+        Okc, Lkc = _prefill(q2, kc, vc, table2, cu2, ctx, bs, causal=True, scale=s,
+                            num_blocks=pool)
+        _close(Okc[-1], Ok[-1], 1e-13, f"dropped block, causal last row bs={bs}")
+        _close(Lkc[-1], Lk[-1], 1e-13, f"dropped block, causal last LSE bs={bs}")
+
+
 # --- N4: residual add + RMS norm ---------------------------------------------------------
 def _norm_rows(seed, M=4, d=37):
     rng = _rng(seed)
@@ -579,7 +648,7 @@ ALL_PINS = [
     pin_rows_sum_to_one, pin_worked_row, pin_online_equals_two_pass, pin_split_merge,
     pin_stability, pin_masked_row, pin_identical_keys, pin_causal_row0, pin_degenerate,
     pin_brute_force, pin_shift_invariance, pin_v_affine, pin_gqa, pin_permutations,
-    pin_decode_paged, pin_norm_residual_is_sum, pin_norm_unit_rms, pin_norm_scale_invariance,
+    pin_decode_paged, pin_prefill_paged, pin_norm_residual_is_sum, pin_norm_unit_rms, pin_norm_scale_invariance,
     pin_norm_constant_and_eps, pin_norm_brute_force, pin_rope_worked,
     pin_rope_rotation_properties, pin_rope_cache_write,
 ]

@@ -112,6 +112,65 @@ def _gather_mutant(kind):
     return gather
 
 
+def _prefill_mutant(kind):
+    """prefill_paged with one planted mistake (the pool check is left out of every mutant but
+    the one that ignores it, which is what the pins exercise it with)."""
+    real = OA.prefill_paged
+
+    def prefill(q, k_cache, v_cache, block_table, cu_seqlens_q, ctx_lens, block_size,
+                causal=True, scale=None, num_blocks=0):
+        if kind == "pool_check_ignored":
+            return real(q, k_cache, v_cache, block_table, cu_seqlens_q, ctx_lens, block_size,
+                        causal=causal, scale=scale, num_blocks=0)
+        if num_blocks > 0:
+            return real(q, k_cache, v_cache, block_table, cu_seqlens_q, ctx_lens, block_size,
+                        causal=causal, scale=scale, num_blocks=num_blocks)
+        T, Hq, D = q.shape
+        O = np.zeros((T, Hq, v_cache.shape[3]))
+        L = np.full((T, Hq), -np.inf)
+        for b in range(len(ctx_lens)):
+            r0, r1 = int(cu_seqlens_q[b]), int(cu_seqlens_q[b + 1])
+            if kind == "rows_shifted":
+                r0, r1 = min(r0 + 1, T), min(r1 + 1, T)
+            n, ctx = r1 - r0, int(ctx_lens[b])
+            if kind == "context_excludes_chunk":
+                ctx -= n
+            if n <= 0 or ctx <= 0:
+                continue
+            qb = np.transpose(q[r0:r1], (1, 0, 2))[None]
+            Kb = OA.gather_paged(k_cache, block_table, ctx, b, block_size)[None]
+            Vb = OA.gather_paged(v_cache, block_table, ctx, b, block_size)[None]
+            if kind == "mask_top_left" and causal:
+                # queries placed at positions 0 .. n-1 instead of the context's last ones
+                Sq = qb.shape[2]
+                pad = np.zeros((1, Hq, ctx - Sq, D)) if ctx > Sq else np.zeros((1, Hq, 0, D))
+                o, lse = OA.attention(np.concatenate([qb, pad], axis=2)[:, :, :max(ctx, Sq)],
+                                      Kb, Vb, causal=True, scale=scale)
+                o, lse = o[:, :, :Sq], lse[:, :, :Sq]
+            else:
+                o, lse = OA.attention(qb, Kb, Vb, causal=causal and kind != "mask_ignored",
+                                      scale=scale)
+            O[r0:r1] = np.transpose(o[0], (1, 0, 2))
+            L[r0:r1] = lse[0].T
+        return O, L
+    return prefill
+
+
+PREFILL_MUTANTS = ["pool_check_ignored", "rows_shifted", "context_excludes_chunk",
+                   "mask_top_left", "mask_ignored"]
+
+
+@pytest.mark.parametrize("kind", PREFILL_MUTANTS)
+def test_prefill_mutant_is_caught(kind, monkeypatch):
+    monkeypatch.setattr(OA, "prefill_paged", _prefill_mutant(kind))
+    assert "pin_prefill_paged" in _some_pin_fails()
+
+
+def test_unmutated_prefill_copy_passes(monkeypatch):
+    monkeypatch.setattr(OA, "prefill_paged", _prefill_mutant("none"))
+    assert _some_pin_fails() == []
+
+
 def _some_pin_fails():
     failed = []
     for pin in pins.ALL_PINS:

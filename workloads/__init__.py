@@ -34,7 +34,9 @@ import numpy as np
 
 __all__ = [
     "FwdConfig", "DecodeConfig", "CONFIGS", "bf16_round", "bf16_bits", "bits_to_f32",
-    "fwd_inputs", "decode_inputs", "DecodeInputs", "sample_rows", "NormConfig", "NORM_CONFIGS",
+    "fwd_inputs", "decode_inputs", "DecodeInputs", "sample_rows", "PagedPrefillInputs",
+    "paged_prefill_inputs", "PagedPrefillConfig", "PAGED_PREFILL_CONFIGS",
+    "paged_prefill_inputs_for", "NormConfig", "NORM_CONFIGS",
     "norm_inputs", "norm_inputs_for", "rope_inputs",
 ]
 
@@ -223,6 +225,78 @@ def decode_inputs(B, Hq, Hkv, D, block_size, ctx_lo, ctx_hi, seed, ctx_lens=None
 def decode_inputs_for(cfg: DecodeConfig, **kw):
     return decode_inputs(cfg.B, cfg.Hq, cfg.Hkv, cfg.D, cfg.block_size, cfg.ctx_lo,
                          cfg.ctx_hi, cfg.seed, **kw)
+
+
+@dataclass
+class PagedPrefillInputs:
+    q: np.ndarray            # [T, Hq, D] float32 (bf16-exact), sequences packed token-major
+    k_cache: np.ndarray      # [num_blocks, Hkv, 16, D] float32 (bf16-exact)
+    v_cache: np.ndarray
+    block_table: np.ndarray  # [B, stride] int32, -1 past a sequence's last block
+    cu_seqlens_q: np.ndarray # [B + 1] int32
+    ctx_lens: np.ndarray     # [B] int32, keys per sequence (its new tokens included)
+    block_size: int
+
+
+def paged_prefill_inputs(Hq, Hkv, D, q_lens, ctx_lens, seed, poison="finite", extra_blocks=0,
+                         table_stride=None):
+    """A chunked-prefill step over a paged cache: sequence b has ctx_lens[b] keys in the cache,
+    of which its last q_lens[b] are the new tokens whose queries are packed into q.
+
+    The cache, block table and poisoned tails are drawn exactly as decode_inputs draws them
+    (same seed); q comes from a second generator seeded with seed + 7919, N(0,1) rounded to
+    bf16. ``table_stride`` widens the table (extra entries -1), as a serving stack that sizes
+    its tables for the longest context does."""
+    B = len(ctx_lens)
+    d = decode_inputs(B, Hq, Hkv, D, 16, 0, 0, seed, ctx_lens=ctx_lens, poison=poison,
+                      extra_blocks=extra_blocks)
+    q_lens = np.asarray(q_lens, dtype=np.int64)
+    assert q_lens.shape == (B,)
+    cu = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
+    rng = np.random.default_rng(seed + 7919)
+    q = _normal(rng, (int(cu[-1]), Hq, D), "bf16", 1.0)
+    table = d.block_table
+    if table_stride is not None and table_stride > table.shape[1]:
+        wide = np.full((B, table_stride), -1, dtype=np.int32)
+        wide[:, :table.shape[1]] = table
+        table = wide
+    return PagedPrefillInputs(q, d.k_cache, d.v_cache, table, cu, d.ctx_lens, 16)
+
+
+@dataclass(frozen=True)
+class PagedPrefillConfig:
+    name: str
+    Hq: int
+    Hkv: int
+    D: int
+    q_lens: tuple
+    ctx_lens: tuple
+    seed: int
+    causal: bool = True
+    kind: str = field(default="paged_prefill")
+
+    @property
+    def scale(self) -> np.float32:
+        return np.float32(1.0 / math.sqrt(self.D))
+
+
+PAGED_PREFILL_CONFIGS = {
+    # the chunked-prefill step through the paged cache: the last 512 tokens of a 4096-token
+    # prompt, whose keys and values (the chunk's included) sit in 16-token blocks of the pool
+    "paged_prefill_512_of_4096": PagedPrefillConfig(
+        "paged_prefill_512_of_4096", Hq=32, Hkv=8, D=128, q_lens=(512,), ctx_lens=(4096,),
+        seed=1010),
+    # a mixed batch of chunks of eight sequences, as a scheduler that batches the prefill
+    # chunks of several requests forms it: chunk lengths and contexts of all sizes, ragged ends
+    "paged_prefill_varlen_b8": PagedPrefillConfig(
+        "paged_prefill_varlen_b8", Hq=32, Hkv=8, D=128,
+        q_lens=(512, 64, 1024, 300, 128, 2048, 17, 707),
+        ctx_lens=(4096, 8192, 1024, 2000, 3000, 2048, 6000, 5000), seed=1011),
+}
+
+
+def paged_prefill_inputs_for(cfg: PagedPrefillConfig, **kw):
+    return paged_prefill_inputs(cfg.Hq, cfg.Hkv, cfg.D, cfg.q_lens, cfg.ctx_lens, cfg.seed, **kw)
 
 
 def sample_rows(B, Hq, Sq, n, seed, must=()):

@@ -368,6 +368,56 @@ def chunked_prefill_timing(A, torch, dev, stream, reps):
             "key_splits": A.attn_fwd_workspace_bytes(1, 32, 8, 512, 4096, 128, True) > 0}
 
 
+def paged_prefill_flops(cfg) -> float:
+    """4*D flops per visible (query, key) pair, summed over the sequences of the batch."""
+    total = 0
+    for n, ctx in zip(cfg.q_lens, cfg.ctx_lens):
+        i = np.arange(n, dtype=np.int64)
+        total += int(np.clip(i + (ctx - n) + 1, 0, ctx).sum()) if cfg.causal else n * ctx
+    return 4.0 * cfg.Hq * cfg.D * total
+
+
+def paged_prefill_timing(A, torch, dev, stream, reps):
+    """Prefill through the paged cache (attn_fwd_paged): the 512-token chunk over a 4096-token
+    context, and a mixed batch of eight sequences' chunks; timed back to back."""
+    out = {}
+    for name, cfg in W.PAGED_PREFILL_CONFIGS.items():
+        x = W.paged_prefill_inputs_for(cfg)
+        bf = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(torch.bfloat16)
+        i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+        q, kc, vc = bf(x.q), bf(x.k_cache), bf(x.v_cache)
+        bt, cu, ctx = i32(x.block_table), i32(x.cu_seqlens_q), i32(x.ctx_lens)
+        o = torch.empty_like(q)
+        lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
+        max_q, max_ctx = max(cfg.q_lens), max(cfg.ctx_lens)
+        call = lambda: A.attn_fwd_paged(q, kc, vc, bt, cu, ctx, max_q, max_ctx,
+                                        causal=cfg.causal, scale=float(cfg.scale), out=o,
+                                        lse=lse)
+        for _ in range(3):
+            call()
+        torch.cuda.synchronize()
+        ev = HipEvents(2)
+        ev.record(0, stream)
+        for _ in range(reps):
+            call()
+        ev.record(1, stream)
+        torch.cuda.synchronize()
+        us = ev.elapsed_ms(0, 1) * 1e3 / reps
+        ev.close()
+        flops = paged_prefill_flops(cfg)
+        tf = flops / (us * 1e-6) / 1e12
+        out[name] = {"workload": f"Hq={cfg.Hq} Hkv={cfg.Hkv} D={cfg.D} chunks {list(cfg.q_lens)} "
+                                 f"over contexts {list(cfg.ctx_lens)}, 16-token blocks, "
+                                 f"{'causal (bottom-right)' if cfg.causal else 'no mask'} bf16",
+                     "us": round(us, 2), "flops_per_launch": flops, "tflops": round(tf, 2),
+                     "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                     "key_splits": A.attn_fwd_paged_workspace_bytes(
+                         len(cfg.q_lens), int(sum(cfg.q_lens)), cfg.Hq, cfg.Hkv, cfg.D, max_q,
+                         max_ctx, cfg.causal) > 0}
+        del q, kc, vc, bt, cu, ctx, o, lse
+    return out
+
+
 class HipGraph:
     """Stream capture into a hipGraph and its launch, through the HIP runtime's own entry points
     (ctypes), so replays cost no framework code on the host."""
@@ -603,6 +653,7 @@ def main():
     rope = rope_timing(A, torch, dev, dq, dkc, dvc, dbt, dctx, flush, flush_sink, stream,
                        args.norm_reps) if args.norm_reps > 0 else None
     chunk = chunked_prefill_timing(A, torch, dev, stream, 20) if args.norm_reps > 0 else None
+    paged = paged_prefill_timing(A, torch, dev, stream, 20) if args.norm_reps > 0 else None
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     flops = prefill_flops(pcfg)
     tflops = flops / (fwd_ms * 1e-3) / 1e12
@@ -670,6 +721,8 @@ def main():
         out["rope_cache_write"] = rope
     if chunk is not None:
         out["chunked_prefill"] = chunk
+    if paged is not None:
+        out["paged_prefill"] = paged
     if args.cpu_seconds > 0:
         progress("timing the fp64 oracle on the host")
         out["cpu_baseline"] = cpu_baseline(args.cpu_seconds, pcfg, *head0)

@@ -17,7 +17,7 @@ import os
 __all__ = [
     "AttnError", "library_path", "load_library",
     "attn_fwd", "attn_fwd_f32", "attn_fwd_ex", "attn_fwd_workspace_bytes", "attn_fwd_force_mapping",
-    "FWD_MAPPINGS", "attn_decode_paged",
+    "FWD_MAPPINGS", "attn_fwd_paged", "attn_fwd_paged_workspace_bytes", "attn_decode_paged",
     "attn_decode_paged_ex", "attn_decode_paged_noalloc", "attn_decode_noalloc_max_bytes",
     "attn_decode_workspace_bytes", "attn_decode_default_workers", "attn_status_string",
     "attn_last_error", "attn_release_workspace", "attn_abi_version", "attn_add_rms_norm",
@@ -35,6 +35,9 @@ _SIGNATURES = {
     "attn_fwd_ex": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P, _Z, _P]),
     "attn_fwd_workspace_bytes": (_Z, [_I, _I, _I, _I, _I, _I, _I]),
     "attn_fwd_force_mapping": (_I, [_I]),
+    "attn_fwd_paged": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I,
+                            _I, _I, _F, _P, _Z, _P]),
+    "attn_fwd_paged_workspace_bytes": (_Z, [_I, _I, _I, _I, _I, _I, _I, _I]),
     "attn_decode_paged": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P]),
     "attn_decode_paged_ex": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I,
                                   _I, _P, _Z, _P]),
@@ -234,6 +237,62 @@ def attn_fwd_f32(q, k, v, causal=False, scale=None, out=None, lse=None, want_lse
     """fp32 forward; same contract as :func:`attn_fwd` with float32 q, k, v, out."""
     return _fwd("attn_fwd_f32", _torch().float32, q, k, v, causal, scale, out, lse, want_lse,
                 stream)
+
+
+def attn_fwd_paged(q, k_cache, v_cache, block_table, cu_seqlens_q, ctx_lens, max_q, max_ctx,
+                   causal=True, scale=None, out=None, lse=None, want_lse=True,
+                   check_blocks=True, workspace=None, stream=None):
+    """Prefill of packed query tokens against a paged KV cache (bf16); returns (out, lse).
+
+    q [T, Hq, D]; k_cache, v_cache [num_blocks, Hkv, 16, D]; block_table [B, stride] int32;
+    cu_seqlens_q [B + 1] int32 (sequence b's tokens are rows cu[b] .. cu[b+1]-1 of q);
+    ctx_lens [B] int32 (each sequence's keys, its new tokens included). ``max_q`` and
+    ``max_ctx`` bound the per-sequence query and key counts (host integers: no
+    synchronisation). The table's row stride is passed as ``block_table.shape[1]``;
+    ``check_blocks`` passes the pool size so out-of-pool entries mask their keys instead of
+    being read. ``workspace``: optional uint8 device tensor of at least
+    attn_fwd_paged_workspace_bytes(...) bytes (None: the library's own)."""
+    torch = _torch()
+    if q.dim() != 3 or k_cache.dim() != 4:
+        raise ValueError("q must be [T, Hq, D] and caches [num_blocks, Hkv, block_size, D]")
+    T, Hq, D = q.shape
+    nb, Hkv, bs, Dk = k_cache.shape
+    if Dk != D or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("cache shapes do not match q")
+    dev = q.device
+    _need(q, "q", torch.bfloat16, dev)
+    _need(k_cache, "k_cache", torch.bfloat16, dev)
+    _need(v_cache, "v_cache", torch.bfloat16, dev)
+    if block_table.dim() != 2:
+        raise ValueError("block_table must be [B, stride]")
+    B = block_table.shape[0]
+    _need(block_table, "block_table", torch.int32, dev)
+    _need(cu_seqlens_q, "cu_seqlens_q", torch.int32, dev, (B + 1,))
+    _need(ctx_lens, "ctx_lens", torch.int32, dev, (B,))
+    if out is None:
+        out = torch.empty((T, Hq, D), dtype=torch.bfloat16, device=dev)
+    _need(out, "out", torch.bfloat16, dev, (T, Hq, D))
+    if lse is None and want_lse:
+        lse = torch.empty((T, Hq), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, dev, (T, Hq))
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8, dev)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    with torch.cuda.device(dev):
+        _check(load_library().attn_fwd_paged(
+            _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(cu_seqlens_q),
+            _ptr(ctx_lens), _ptr(out), _ptr(lse), B, T, Hq, Hkv, D, bs, int(max_q),
+            int(max_ctx), int(block_table.shape[1]), int(nb) if check_blocks else 0,
+            1 if causal else 0, float(scale), _ptr(workspace),
+            int(workspace.numel()) if workspace is not None else 0, _stream_ptr(dev, stream)))
+    return out, lse
+
+
+def attn_fwd_paged_workspace_bytes(B, T, Hq, Hkv, D, max_q, max_ctx, causal=True) -> int:
+    return load_library().attn_fwd_paged_workspace_bytes(B, T, Hq, Hkv, D, max_q, max_ctx,
+                                                         1 if causal else 0)
 
 
 def _decode_checks(q, k_cache, v_cache, block_table, ctx_lens):

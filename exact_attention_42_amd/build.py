@@ -31,6 +31,7 @@ HIPCC_FLAGS = [
 # needs a canonicalising v_max first, which halves the row-max cost of the softmax.
 FILE_FLAGS = {
     "attn_fwd_bf16.hip": ["-fno-honor-nans"],
+    "attn_fwd_paged.hip": ["-fno-honor-nans"],
     # the decode kernel needs few registers; with the accumulators in ordinary VGPRs the
     # per-block rescale runs on them directly instead of copying through AGPRs
     "attn_decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],

@@ -246,6 +246,67 @@ int run_fwd(bool f32, const void* q, const void* k, const void* v, void* o, floa
   return ok();
 }
 
+int run_fwd_paged(const void* q, const void* k_cache, const void* v_cache,
+                  const int32_t* block_table, const int32_t* cu_seqlens_q,
+                  const int32_t* ctx_lens, void* o, float* lse, int B, int T, int Hq, int Hkv,
+                  int D, int block_size, int max_q, int max_ctx, int table_stride,
+                  int num_blocks, int causal, float scale, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+  if (B < 0 || T < 0 || max_q < 0 || max_ctx < 0)
+    return fail(ATTN_ERR_SHAPE, "B, T, max_q and max_ctx must be >= 0 (B=%d T=%d max_q=%d "
+                "max_ctx=%d)", B, T, max_q, max_ctx);
+  if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0)
+    return fail(ATTN_ERR_SHAPE, "need Hq >= 1, Hkv >= 1 and Hq %% Hkv == 0 (Hq=%d Hkv=%d)",
+                Hq, Hkv);
+  if (table_stride < 1)
+    return fail(ATTN_ERR_SHAPE, "table_stride must be >= 1 (got %d)", table_stride);
+  if ((long long)B * Hq > 0x7fffffffLL || (long long)T * Hq > 0x7fffffffLL ||
+      max_q > (1 << 30) || max_ctx > (1 << 30) || (long long)B * table_stride > 0x7fffffffLL)
+    return fail(ATTN_ERR_SHAPE, "problem too large (B*Hq=%lld T*Hq=%lld max_q=%d max_ctx=%d)",
+                (long long)B * Hq, (long long)T * Hq, max_q, max_ctx);
+  if (D != 64 && D != 128)
+    return fail(ATTN_ERR_UNSUPPORTED, "head dimension D=%d not supported (64 or 128)", D);
+  if (block_size != 16)
+    return fail(ATTN_ERR_UNSUPPORTED, "block_size=%d not supported (16)", block_size);
+  if (int rc = check_scale(scale)) return rc;
+  if (B == 0 || T == 0 || max_q == 0) return ok();
+  if (!q || !k_cache || !v_cache || !block_table || !cu_seqlens_q || !ctx_lens || !o)
+    return fail(ATTN_ERR_NULL, "q, k_cache, v_cache, block_table, cu_seqlens_q, ctx_lens and o "
+                "must not be NULL");
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(o, 16))
+    return fail(ATTN_ERR_ALIGN, "q, k_cache, v_cache and o must be 16-byte aligned");
+  if (!aligned(block_table, 4) || !aligned(cu_seqlens_q, 4) || !aligned(ctx_lens, 4) ||
+      (lse && !aligned(lse, 4)))
+    return fail(ATTN_ERR_ALIGN, "block_table, cu_seqlens_q, ctx_lens and lse must be 4-byte "
+                "aligned");
+  attn::PagedProblem p{};
+  p.q = q; p.k_cache = k_cache; p.v_cache = v_cache; p.block_table = block_table;
+  p.cu_seqlens_q = cu_seqlens_q; p.ctx_lens = ctx_lens; p.o = o; p.lse = lse;
+  p.B = B; p.T = T; p.Hq = Hq; p.Hkv = Hkv; p.D = D; p.max_q = max_q; p.max_ctx = max_ctx;
+  p.table_stride = table_stride; p.num_blocks = num_blocks; p.causal = causal ? 1 : 0;
+  p.scale = scale;
+  p.nsplit = attn::fwd_paged_splits(p, device_cus());
+  p.workspace = nullptr;
+  std::unique_lock<std::mutex> ws_lock(g_ws_mutex, std::defer_lock);
+  if (p.nsplit > 1) {
+    const size_t need = attn::fwd_paged_workspace_bytes(p, p.nsplit);
+    if (workspace) {
+      if (workspace_bytes < need)
+        return fail(ATTN_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed",
+                    workspace_bytes, need);
+      if (!aligned(workspace, 16))
+        return fail(ATTN_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+      p.workspace = workspace;
+    } else {
+      ws_lock.lock();
+      if (int rc = get_workspace_locked(stream, need, &p.workspace)) return rc;
+    }
+  }
+  hipError_t e = attn::launch_fwd_paged(p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "attn_fwd_paged launch");
+  return ok();
+}
+
 int run_decode(const void* q, const void* k_cache, const void* v_cache,
                const int32_t* block_table, const int32_t* ctx_lens, void* o, float* lse, int B,
                int Hq, int Hkv, int D, int block_size, float scale, int table_stride,
@@ -416,6 +477,29 @@ size_t attn_fwd_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk, int D, i
   return attn::fwd_bf16_workspace_bytes(p, attn::fwd_bf16_splits(p, device_cus()));
 }
 
+int attn_fwd_paged(const void* q, const void* k_cache, const void* v_cache,
+                   const int32_t* block_table, const int32_t* cu_seqlens_q,
+                   const int32_t* ctx_lens, void* o, float* lse, int B, int T, int Hq, int Hkv,
+                   int D, int block_size, int max_q, int max_ctx, int table_stride,
+                   int num_blocks, int causal, float scale, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  return run_fwd_paged(q, k_cache, v_cache, block_table, cu_seqlens_q, ctx_lens, o, lse, B, T,
+                       Hq, Hkv, D, block_size, max_q, max_ctx, table_stride, num_blocks, causal,
+                       scale, workspace, workspace_bytes, stream);
+}
+
+size_t attn_fwd_paged_workspace_bytes(int B, int T, int Hq, int Hkv, int D, int max_q,
+                                      int max_ctx, int causal) {
+  if (B < 0 || T < 0 || max_q < 0 || max_ctx < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 ||
+      (D != 64 && D != 128) || (long long)B * Hq > 0x7fffffffLL ||
+      (long long)T * Hq > 0x7fffffffLL || max_q > (1 << 30) || max_ctx > (1 << 30))
+    return 0;
+  attn::PagedProblem p{};
+  p.B = B; p.T = T; p.Hq = Hq; p.Hkv = Hkv; p.D = D; p.max_q = max_q; p.max_ctx = max_ctx;
+  p.causal = causal ? 1 : 0;
+  return attn::fwd_paged_workspace_bytes(p, attn::fwd_paged_splits(p, device_cus()));
+}
+
 int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
                       const int32_t* block_table, const int32_t* ctx_lens, void* o, int B,
                       int Hq, int Hkv, int D, int block_size, float scale, void* stream) {
@@ -489,6 +573,6 @@ void attn_release_workspace(void) {
   if (have_cur) (void)hipSetDevice(cur);
 }
 
-int attn_abi_version(void) { return 8; }
+int attn_abi_version(void) { return 9; }
 
 }  // extern "C"

@@ -54,130 +54,12 @@ namespace {
 
 using namespace cdna4;
 
-constexpr int kBM = 128;           // query rows per tile
 constexpr int kWideRows = 256;     // query rows per workgroup of the wide kernel
 // Pair kernel is used for causal launches with at most this many tiles per head.
 constexpr int kPairMaxTiles = 64;
 // Most key-range splits per query tile (the split path serves few-tile problems, such as a
 // prefill chunk against a long prefix, whose query tiles alone would leave CUs idle).
 constexpr int kMaxFwdSplits = 8;
-
-// O^T += V^T P^T for the first NKB 32-key blocks of the tile. Slots (h, 0..3) of P^T hold
-// keys 32kb+16t+4h+{0..3} and slots (h, 4..7) the same + 8: one transposed read each.
-template <int D, int NKB>
-__device__ __forceinline__ void pv_blocks(WaveState<D>& w, const char* sv,
-                                          const u32x4 (&pb)[2][2]) {
-  using G = Geo<D, 4>;
-#pragma unroll
-  for (int db = 0; db < G::DB; ++db) {
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const char* vp = sv + w.voff[db] + (32 * kb + 16 * t) * G::kRow;
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vp));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vp + 8 * G::kRow));
-        const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
-        const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
-        w.o[db] = mfma32x32x16(u32x4{l2[0], l2[1], h2[0], h2[1]}, pb[kb][t], w.o[db]);
-      }
-    }
-  }
-}
-
-// One K/V tile: S^T = K Q^T, mask, online softmax, O^T += V^T P^T.
-template <int D, bool CAUSAL>
-__device__ __forceinline__ void compute_tile(WaveState<D>& w, const char* sk, const char* sv,
-                                             int kt, int Sk, int qw, int wave_last_key,
-                                             int my_q, int off, int h, float c) {
-  using G = Geo<D, 4>;
-  bool act[2];
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-    act[kb] = (kt + 32 * kb < Sk) && (!CAUSAL || kt + 32 * kb <= wave_last_key);
-
-  // ---- S^T = K Q^T ----
-  // (computed for every block: a block no query of this wave can see is masked below, and
-  //  skipping it would cost a register copy of every score on all the other tiles)
-  u32x4 kf[2][G::KS];
-#pragma unroll
-  for (int kk = 0; kk < G::KS; ++kk)
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-      kf[kb][kk] = *reinterpret_cast<const u32x4*>(sk + 32 * kb * G::kRow + w.koff[kk]);
-  f32x16 s[2];
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32x32x16(kf[kb][0], w.qf[0], f32x16{});
-#pragma unroll
-  for (int kk = 1; kk < G::KS; ++kk)
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32x32x16(kf[kb][kk], w.qf[kk], s[kb]);
-
-  // ---- mask: causal diagonal, key tail, inactive blocks ----
-  const bool need_mask = (kt + kBN > Sk) || (CAUSAL && kt + kBN - 1 > qw + off);
-  if (need_mask) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = kt + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
-        bool vis = act[kb] && key < Sk;
-        if (CAUSAL) vis = vis && (key <= my_q + off);
-        s[kb][r] = vis ? s[kb][r] : -INFINITY;
-      }
-    }
-  }
-
-  // ---- online softmax (per lane = per query) with a lazily moved reference ----
-  float mx = -INFINITY;
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int r = 0; r < 16; r += 2) mx = fmax3(mx, s[kb][r], s[kb][r + 1]);
-  mx = xor32_max(mx);
-  const float mxc = mx * c;                       // -inf stays -inf (c > 0)
-  const bool move = mxc > w.mref + kLazy;
-  if (__builtin_amdgcn_ballot_w64(move)) {
-    // (the empty asm keeps this a branch: folded into straight-line code, the 64 multiplies
-    //  below would run on every tile)
-    asm volatile("");
-    // lanes that keep their reference use 1 (not exp2(mref - mref): NaN while mref = -inf);
-    // a lane moving away from -inf gets 0, which clears its empty state
-    const float alpha = move ? exp2_fast(w.mref - mxc) : 1.f;
-    w.mref = move ? mxc : w.mref;
-    w.l_run *= alpha;
-#pragma unroll
-    for (int i = 0; i < G::DB; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) w.o[i][r] *= alpha;
-  }
-  const float mu = (w.mref == -INFINITY) ? 0.f : w.mref;
-
-  // ---- P^T as bf16 B operands; fp32 row sums (the LSE needs them unrounded) ----
-  u32x4 pb[2][2];
-  float ls[2];
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float p0 = exp2_fast(__builtin_fmaf(s[kb][8 * t + 2 * e], c, -mu));
-        const float p1 = exp2_fast(__builtin_fmaf(s[kb][8 * t + 2 * e + 1], c, -mu));
-        if (kb == 0 && t == 0 && e == 0) {
-          ls[0] = p0;
-          ls[1] = p1;
-        } else {
-          ls[0] += p0;
-          ls[1] += p1;
-        }
-        pb[kb][t][e] = pack_bf16x2(p0, p1);
-      }
-  w.l_run += ls[0] + ls[1];
-
-  // ---- O^T += V^T P^T over the active 32-key blocks (a uniform choice per tile) ----
-  pv_blocks<D, 2>(w, sv, pb);
-}
 
 // SPLIT: the workgroup covers one of a.nsplit contiguous ranges of the query tile's key tiles
 // and writes its unnormalised partial result (O, reference max, sum) to the workspace; the
@@ -719,37 +601,6 @@ __device__ __forceinline__ void fwd_pair_pipe_body(const FwdArgs& a) {
     }
   }
   if (!lwave) store_rows(qw);
-}
-
-// Merges the key-range splits of each query row: M = max m_s, L = sum l_s 2^(m_s - M),
-// O = sum O_s 2^(m_s - M) / L (the online-softmax merge), then O in bf16 and the natural-log
-// LSE. D/4 threads per row, each with 4 consecutive columns.
-template <int D>
-__device__ __forceinline__ void fwd_split_combine_body(const FwdArgs& a) {
-  constexpr int TPR = D / 4;
-  const size_t nrows = (size_t)a.B * a.Hq * a.Sq;
-  const size_t row = (size_t)blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
-  const int c4 = (threadIdx.x % TPR) * 4;
-  if (row >= nrows) return;
-  float M = -INFINITY;
-  for (int s = 0; s < a.nsplit; ++s) M = fmaxf(M, a.part_ml[((size_t)s * nrows + row) * 2]);
-  float L = 0.f;
-  f32x4 O = f32x4{};
-  if (M != -INFINITY) {
-    for (int s = 0; s < a.nsplit; ++s) {
-      const size_t pr = (size_t)s * nrows + row;
-      const f32x2 ml = *reinterpret_cast<const f32x2*>(a.part_ml + pr * 2);
-      if (ml[0] == -INFINITY) continue;
-      const float wgt = exp2_fast(ml[0] - M);
-      L += wgt * ml[1];
-      O += wgt * *reinterpret_cast<const f32x4*>(a.part_o + pr * D + c4);
-    }
-  }
-  const float inv = (L > 0.f) ? 1.f / L : 0.f;
-  u32x2 v = {pack_bf16x2(O[0] * inv, O[1] * inv), pack_bf16x2(O[2] * inv, O[3] * inv)};
-  *reinterpret_cast<u32x2*>(a.o + row * D + c4) = v;
-  if (a.lse != nullptr && c4 == 0)
-    a.lse[row] = (L > 0.f) ? (M + log2_fast(L)) * kLn2 : -INFINITY;
 }
 
 template <int D, bool CAUSAL>

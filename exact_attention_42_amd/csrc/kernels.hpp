@@ -41,6 +41,30 @@ hipError_t launch_fwd_bf16_wide(const FwdProblem& p, hipStream_t stream);
 // fp32 Q/K/V/O, fp32 LSE; vector-ALU kernel. D in {64, 128}.
 hipError_t launch_fwd_f32(const FwdProblem& p, hipStream_t stream);
 
+// Prefill of packed query tokens against a paged KV cache (several sequences of any lengths).
+struct PagedProblem {
+  const void* q;               // [T, Hq, D] bf16, sequence b's tokens at rows cu_seqlens_q[b..b+1)
+  const void* k_cache;         // [num_blocks, Hkv, 16, D] bf16
+  const void* v_cache;
+  const int32_t* block_table;  // [B, table_stride]
+  const int32_t* cu_seqlens_q; // [B + 1]
+  const int32_t* ctx_lens;     // [B] keys of each sequence (its new tokens included)
+  void* o;                     // [T, Hq, D] bf16
+  float* lse;                  // [T, Hq] fp32 or null
+  int B, T, Hq, Hkv, D;
+  int max_q, max_ctx;          // bounds on the query tokens and keys of any one sequence
+  int table_stride;
+  int num_blocks;              // <= 0: block ids unchecked
+  int causal;
+  float scale;
+  int nsplit;                  // key-range splits per query tile (<= 1: none)
+  void* workspace;             // nsplit > 1: fwd_paged_workspace_bytes(p, nsplit) bytes
+};
+
+int fwd_paged_splits(const PagedProblem& p, int cus);
+size_t fwd_paged_workspace_bytes(const PagedProblem& p, int nsplit);
+hipError_t launch_fwd_paged(const PagedProblem& p, hipStream_t stream);
+
 struct DecodeProblem {
   const void* q;            // [B, Hq, D] bf16
   const void* k_cache;      // [num_blocks, Hkv, block_size, D] bf16

@@ -106,6 +106,48 @@ int attn_fwd_f32(const void* q, const void* k, const void* v, void* o, float* ls
                  int B, int Hq, int Hkv, int Sq, int Sk, int D,
                  int causal, float scale, void* stream);
 
+/* Prefill over a paged KV cache, for several sequences of any lengths at once (a chunked
+ * prefill: the new tokens of each sequence attend to its whole cached context). Prefill and
+ * decode are two schedules of the same attention ("Kernel Fusion, Softmax, and Attention");
+ * the cache is the paged one of "Optimizing Large Language Model Inference ...", §Paged
+ * Attention and Dynamic KV Cache Management, which attn_rope_cache_write fills.
+ *   q, o:      [T, Hq, D] bfloat16, token-major; sequence b's query tokens are rows
+ *              cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1
+ *   lse:       [T, Hq] float32, or NULL
+ *   k_cache, v_cache: [num_blocks, Hkv, block_size, D] bfloat16; key t of sequence b is slot
+ *              t % block_size of physical block block_table[b * table_stride + t / block_size]
+ *   block_table: [B, table_stride] int32
+ *   cu_seqlens_q: [B + 1] int32, nondecreasing, cu_seqlens_q[B] <= T
+ *   ctx_lens:  [B] int32, keys of each sequence in the cache, its own query tokens included
+ *              (they are its last cu_seqlens_q[b+1] - cu_seqlens_q[b] keys)
+ * Query i of sequence b is at position ctx_lens[b] - n_b + i (n_b its query count); causal != 0
+ * lets it see keys 0 .. that position (the bottom-right alignment of attn_fwd), causal == 0
+ * all ctx_lens[b] keys. A row that sees no key gets O = 0 and LSE = -inf.
+ *   max_q:     an upper bound on n_b (sizes the grid; a longer sequence is still done whole,
+ *              by fewer workgroups); max_q == 0 launches nothing
+ *   max_ctx:   an upper bound on ctx_lens[b] (with max_q, decides the key-range splits)
+ *   num_blocks: pool size; > 0 makes a table entry outside [0, num_blocks) mask its block's
+ *              keys (they take no part) instead of being read; <= 0 = unchecked
+ * Keys at or past table_stride * block_size have no table entry and are masked the same way.
+ * Cache rows past ctx_lens[b] are never read, whatever they hold.
+ * A sequence whose row range is invalid (cu_seqlens_q[b] < 0, decreasing, or past T) is
+ * skipped; rows of q outside [cu_seqlens_q[0], cu_seqlens_q[B]) are not written.
+ * Few query tiles (a short chunk) split each tile's keys into up to 8 ranges whose partial
+ * results a second kernel merges; the partials go to workspace (caller-owned, 16-byte aligned,
+ * at least attn_fwd_paged_workspace_bytes(...) bytes) or, when workspace is NULL, to the
+ * library workspace (see above). block_size must be 16, D 64 or 128. */
+int attn_fwd_paged(const void* q, const void* k_cache, const void* v_cache,
+                   const int32_t* block_table, const int32_t* cu_seqlens_q,
+                   const int32_t* ctx_lens, void* o, float* lse, int B, int T, int Hq, int Hkv,
+                   int D, int block_size, int max_q, int max_ctx, int table_stride,
+                   int num_blocks, int causal, float scale, void* workspace,
+                   size_t workspace_bytes, void* stream);
+
+/* Workspace bytes attn_fwd_paged needs for these sizes (0 when it does not split, or for
+ * invalid arguments). */
+size_t attn_fwd_paged_workspace_bytes(int B, int T, int Hq, int Hkv, int D, int max_q,
+                                      int max_ctx, int causal);
+
 /* One-token decode over a paged KV cache ("Optimizing Large Language Model Inference ...",
  * §Paged Attention and Dynamic KV Cache Management: fixed-size blocks of the cache are placed
  * anywhere in a physical pool and a block table maps each sequence's logical blocks to them).
@@ -234,7 +276,7 @@ const char* attn_last_error(void);
  * that hold them). No call may be running or enqueued-and-unfinished when it is called. */
 void attn_release_workspace(void);
 
-/* ABI version of this header: 8. */
+/* ABI version of this header: 9. */
 int attn_abi_version(void);
 
 #ifdef __cplusplus

@@ -42,7 +42,7 @@ def test_status_strings_and_version():
     for code in range(9):
         assert A.attn_status_string(code) not in ("", "unknown status")
     assert A.attn_status_string(99) == "unknown status"
-    assert A.attn_abi_version() == 8
+    assert A.attn_abi_version() == 9
 
 
 def fwd(*, q=P, k=P, v=P, o=P, lse=0, B=1, Hq=32, Hkv=8, Sq=128, Sk=128, D=128, causal=1,
@@ -78,6 +78,55 @@ def test_fwd_bf16_rejects_a_head_over_2gib():
 def test_fwd_empty_problem_is_a_no_op(kw):
     assert fwd(**kw) == OK
     assert A.attn_last_error() == ""
+
+
+def fwdp(*, q=P, kc=P, vc=P, table=P, cu=P, ctx=P, o=P, lse=0, B=1, T=512, Hq=32, Hkv=8, D=128,
+         bs=16, max_q=512, max_ctx=4096, stride=256, nblocks=0, causal=1, scale=0.08, ws=P,
+         ws_bytes=1 << 40):
+    return A.load_library().attn_fwd_paged(q, kc, vc, table, cu, ctx, o, lse, B, T, Hq, Hkv, D,
+                                           bs, max_q, max_ctx, stride, nblocks, causal, scale,
+                                           ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), NULL), (dict(kc=0), NULL), (dict(vc=0), NULL), (dict(table=0), NULL),
+    (dict(cu=0), NULL), (dict(ctx=0), NULL), (dict(o=0), NULL), (dict(B=-1), SHAPE),
+    (dict(T=-1), SHAPE), (dict(max_q=-1), SHAPE), (dict(max_ctx=-2), SHAPE), (dict(Hq=0), SHAPE),
+    (dict(Hq=32, Hkv=5), SHAPE), (dict(stride=0), SHAPE), (dict(T=1 << 27, Hq=32), SHAPE),
+    (dict(B=1 << 20, stride=1 << 12), SHAPE), (dict(D=96), UNSUP), (dict(bs=32), UNSUP),
+    (dict(q=P + 8), ALIGN), (dict(kc=P + 4), ALIGN), (dict(vc=P + 2), ALIGN),
+    (dict(o=P + 2), ALIGN), (dict(table=P + 2), ALIGN), (dict(cu=P + 1), ALIGN),
+    (dict(ctx=P + 2), ALIGN), (dict(lse=P + 2), ALIGN), (dict(scale=NAN), SCALE),
+    (dict(scale=-1.0), SCALE), (dict(ws_bytes=100), WS), (dict(ws=P + 4), WS),
+])
+def test_fwd_paged_rejects(kw, code):
+    # (the default shape, a 512-token chunk over a 4096-token context, splits its keys, so the
+    #  workspace checks run too)
+    assert fwdp(**kw) == code
+    assert A.attn_last_error() != ""
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(T=0), dict(max_q=0),
+                                dict(B=0, q=0, kc=0, vc=0, table=0, cu=0, ctx=0, o=0)])
+def test_fwd_paged_empty_problem_is_a_no_op(kw):
+    assert fwdp(**kw) == OK
+    assert A.attn_last_error() == ""
+
+
+def test_fwd_paged_workspace_size():
+    # 128 query tiles on 256 CUs: ceil(2 * 256 / 128) = 4 key ranges per tile, each of the
+    # T * Hq rows with D + 2 floats per range
+    if A.attn_fwd_paged_workspace_bytes(1, 512, 32, 8, 128, 512, 4096, 1) == 0:
+        pytest.skip("device reports other than 256 CUs")
+    assert A.attn_fwd_paged_workspace_bytes(1, 512, 32, 8, 128, 512, 4096, 1) == \
+        4 * 512 * 32 * 130 * 4
+    # enough query tiles: no splits
+    assert A.attn_fwd_paged_workspace_bytes(8, 32768, 32, 8, 128, 4096, 4096, 1) == 0
+    for bad in [(-1, 1, 1, 1, 64, 1, 1, 1), (1, 1, 6, 4, 64, 1, 1, 1), (1, 1, 1, 1, 80, 1, 1, 1),
+                (1, 1, 1, 1, 64, -1, 1, 1)]:
+        assert A.attn_fwd_paged_workspace_bytes(*bad) == 0, bad
+    need = A.attn_fwd_paged_workspace_bytes(1, 512, 32, 8, 128, 512, 4096, 1)
+    assert fwdp(ws_bytes=need - 1) == WS
 
 
 def dec(*, q=P, kc=P, vc=P, table=P, ctx=P, o=P, lse=0, B=64, Hq=32, Hkv=8, D=128, bs=16,

@@ -258,7 +258,7 @@ __device__ __forceinline__ void wide_iter(WideWave<D>& w, WidePipe<D>& p, const 
   stretch_end();
 
   // ---- 1b ---- (the mask, rare, between the stretches)
-  if (mask) mask_block(s0, w.lim[0], k0, h);
+  if (__builtin_expect(mask, 0)) mask_block(s0, w.lim[0], k0, h);
   stretch_end();
   f32x16 s1 = f32x16{};
   RowMax r0;
@@ -285,7 +285,7 @@ __device__ __forceinline__ void wide_iter(WideWave<D>& w, WidePipe<D>& p, const 
   stretch_end();
   // (rare) group 0's reference moves: before its exponentials below
   float alpha0 = 1.f;
-  if (any0) alpha0 = apply_move(w.m[0], w.l[0], w.thr[0], r0.mx, move0, c, inv_c);
+  if (__builtin_expect(any0, 0)) alpha0 = apply_move(w.m[0], w.l[0], w.thr[0], r0.mx, move0, c, inv_c);
   const float mu0 = w.m[0];
   stretch_end();
 
@@ -310,7 +310,7 @@ __device__ __forceinline__ void wide_iter(WideWave<D>& w, WidePipe<D>& p, const 
   stretch_end();
 
   // ---- 2b ---- (the mask, rare, between the stretches)
-  if (mask) mask_block(s1, w.lim[1], k0, h);
+  if (__builtin_expect(mask, 0)) mask_block(s1, w.lim[1], k0, h);
   stretch_end();
   // (the current K fragments were last used in 1b: the next block's go into the same registers)
   read_k<D>(w, knext, p.kf);
@@ -337,11 +337,11 @@ __device__ __forceinline__ void wide_iter(WideWave<D>& w, WidePipe<D>& p, const 
   stretch_end();
 
   // ---- rescale (rare), after the products of block i-1 were added ----
-  if (any0) {
+  if (__builtin_expect(any0, 0)) {
 #pragma unroll
     for (int db = 0; db < G::DB; ++db) scale_acc(w.o[0][db], alpha0);
   }
-  if (any1) {
+  if (__builtin_expect(any1, 0)) {
     const float alpha1 = apply_move(w.m[1], w.l[1], w.thr[1], r1.mx, move1, c, inv_c);
 #pragma unroll
     for (int db = 0; db < G::DB; ++db) scale_acc(w.o[1][db], alpha1);
@@ -373,19 +373,40 @@ __device__ __forceinline__ void wide_drain(WideWave<D>& w, WidePipe<D>& p, const
   for (int i = 0; i < NV; ++i) w.o[1][i >> 1] = mfma32x32x16(vf[i], p1[i & 1], w.o[1][i >> 1]);
 }
 
-// Work item -> (query tile rank, batch * query head). The items are ordered KV head by KV head
-// (all query tiles and query heads reading one K/V), heaviest tile first within a KV head, the
-// query heads of a tile together; XCD x (workgroups are dispatched to the 8 XCDs round robin)
-// takes a contiguous run of that order, so the workgroups running at once on an XCD read the K/V
-// of one or two KV heads through its L2.
-__device__ __forceinline__ void wide_item(int id, int nitems, int ntq, int group, int& rank,
-                                          int& bh) {
+// Work item -> (query tile rank, batch * query head). Workgroups are dispatched to the 8 XCDs
+// round robin (workgroup id mod 8), and each XCD (one L2) works through its own KV heads: when
+// the B * Hkv KV heads split evenly, XCD x takes KV heads x * n .. x * n + n - 1, in bundles of
+// ceil(8 / group) consecutive ones; within a bundle the items go tile rank by tile rank,
+// heaviest first, each rank listing all query heads of the bundle. So the workgroups running
+// at once on an XCD read the K/V of a few KV heads through its L2, and at least 8 consecutive
+// workgroups of an XCD's queue have the same amount of work. (Within an XCD the hardware hands
+// workgroups to its shader engines in a fixed rotation and in order: a workgroup whose engine
+// has no free CU holds back the ones behind it, so when heavy and light tiles alternate in the
+// queue, CUs wait for their next workgroup; equal neighbours avoid that.) Otherwise the items
+// are ordered KV head by KV head (heaviest tile first, the query heads of a tile together) and
+// XCD x takes a contiguous eighth of that order.
+__device__ __forceinline__ void wide_item(int id, int nitems, int ntq, int group, int nkv,
+                                          int& rank, int& bh) {
+  constexpr int kXcd = 8;
+  if (nkv % kXcd == 0) {
+    const int x = id % kXcd, j = id / kXcd;
+    const int hpx = nkv / kXcd;                     // KV heads of this XCD
+    const int nb = (kXcd + group - 1) / group;      // KV heads per bundle
+    const int per_bundle = nb * group * ntq;
+    const int bundle = j / per_bundle;
+    const int nbb = min(nb, hpx - bundle * nb);     // KV heads in this bundle (the last: fewer)
+    const int r = j - bundle * per_bundle;
+    rank = r / (nbb * group);
+    const int rem = r - rank * (nbb * group);       // (KV head in bundle) * group + g
+    bh = (x * hpx + bundle * nb) * group + rem;     // (b * Hkv + hk) * group + g = b * Hq + hq
+    return;
+  }
   const int item = xcd_item(id, nitems);
   const int per_kv = group * ntq;
-  const int kvh = item / per_kv;                  // batch * Hkv + KV head
+  const int kvh = item / per_kv;                    // batch * Hkv + KV head
   const int r = item - kvh * per_kv;
   rank = r / group;
-  bh = kvh * group + (r - rank * group);          // (b * Hkv + hk) * group + g = b * Hq + hq
+  bh = kvh * group + (r - rank * group);
 }
 
 template <int D, bool CAUSAL>
@@ -411,7 +432,7 @@ __device__ __forceinline__ void fwd_wide_body(const FwdArgs& a) {
   const int h = lane >> 5;
 
   int rank, bh;
-  wide_item(blockIdx.x, a.nitems, a.ntq, a.group, rank, bh);
+  wide_item(blockIdx.x, a.nitems, a.ntq, a.group, a.B * a.Hkv, rank, bh);
   const int tile = CAUSAL ? (a.ntq - 1 - rank) : rank;
   const int b = bh / a.Hq;
   const int hq = bh - b * a.Hq;
@@ -526,7 +547,7 @@ __device__ __forceinline__ void fwd_wide_body(const FwdArgs& a) {
   // loads were all issued before tile T + 2's 8) and nobody reads the stage of tile T - 1 any more
   auto mid_for = [&](int T) {
     return [&, T]() {
-      if (T + 1 >= nt) return;
+      if (__builtin_expect(T + 1 >= nt, 0)) return;
       __builtin_amdgcn_s_waitcnt(kWaitVm8);
       __builtin_amdgcn_s_barrier();
     };
@@ -564,14 +585,14 @@ __device__ __forceinline__ void fwd_wide_body(const FwdArgs& a) {
     };
     auto mid = mid_for(T);
     const int i = 2 * T;
-    if (i < nblk) {
+    if (__builtin_expect(i < nblk, 1)) {
       wide_iter<D, true>(w, p, vp + 32 * G::kRow, kc + 32 * G::kRow, k0, i >= nunm, h, c,
                          a_inv_c, nothing, hook0);
     } else {
 #pragma unroll
       for (int j = 3; j < kParts; ++j) dma.issue_part_unclamped(k2, v2, kt2, j);
     }
-    if (i + 1 < nblk) {
+    if (__builtin_expect(i + 1 < nblk, 1)) {
       wide_iter<D, false>(w, p, vc, kn, k0 + 32, i + 1 >= nunm, h, c, a_inv_c, mid, hook1);
     } else {
       mid();
@@ -582,11 +603,11 @@ __device__ __forceinline__ void fwd_wide_body(const FwdArgs& a) {
 
   for (int T = 0; T < nt; T += kStages) {
     run_tile(std::integral_constant<int, 0>{}, T);
-    if (T + 1 >= nt) break;
+    if (__builtin_expect(T + 1 >= nt, 0)) break;
     run_tile(std::integral_constant<int, 1>{}, T + 1);
-    if (T + 2 >= nt) break;
+    if (__builtin_expect(T + 2 >= nt, 0)) break;
     run_tile(std::integral_constant<int, 2>{}, T + 2);
-    if (T + 3 >= nt) break;
+    if (__builtin_expect(T + 3 >= nt, 0)) break;
     run_tile(std::integral_constant<int, 3>{}, T + 3);
   }
   // The last block's pending work. Its V tile (tile (nblk - 1) / 2, within the last 4 tiles

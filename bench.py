@@ -294,6 +294,37 @@ def norm_timing(A, torch, dev, flush, flush_sink, stream, reps):
     return res
 
 
+def floor_timing(torch, dev, flush, flush_sink, stream, reps):
+    """The floor the small kernels sit on, timed exactly as they are (alone between fence-free
+    events, after the read flush): a kernel that writes one element, and torch's device copies
+    of 4 MiB (the size of the 64 x 8192 norm's traffic) and 48 MiB (the 2048-token RoPE chunk's)."""
+    one = torch.zeros(1, device=dev)
+    bufs = {}
+    for mib in (4, 48):
+        a = torch.zeros((mib << 20) // 4, device=dev)
+        bufs[mib] = (a, torch.empty_like(a))
+    cases = [("fill_1_element_us", lambda: one.fill_(1.0)),
+             ("device_copy_4MiB_us", lambda: bufs[4][1].copy_(bufs[4][0])),
+             ("device_copy_48MiB_us", lambda: bufs[48][1].copy_(bufs[48][0]))]
+    out = {}
+    for name, fn in cases:
+        fn()
+        torch.cuda.synchronize()
+        ev = HipEvents(2 * reps)
+        for i in range(reps):
+            if flush is not None:
+                torch.amax(flush, dim=0, out=flush_sink)
+            ev.record(2 * i, stream)
+            fn()
+            ev.record(2 * i + 1, stream)
+        torch.cuda.synchronize()
+        out[name] = round(float(np.median([ev.elapsed_ms(2 * i, 2 * i + 1)
+                                           for i in range(reps)])) * 1e3, 2)
+        ev.close()
+    del bufs, one
+    return out
+
+
 def rope_timing(A, torch, dev, dq, dkc, dvc, dbt, dctx, flush, flush_sink, stream, reps):
     """The fused RoPE + paged cache store: (1) the decode step's 64 new tokens (one per
     sequence, at position ctx - 1, into the decode workload's own cache: the step that
@@ -652,6 +683,8 @@ def main():
         if args.norm_reps > 0 else None
     rope = rope_timing(A, torch, dev, dq, dkc, dvc, dbt, dctx, flush, flush_sink, stream,
                        args.norm_reps) if args.norm_reps > 0 else None
+    floor = floor_timing(torch, dev, flush, flush_sink, stream, args.norm_reps) \
+        if args.norm_reps > 0 else None
     chunk = chunked_prefill_timing(A, torch, dev, stream, 20) if args.norm_reps > 0 else None
     paged = paged_prefill_timing(A, torch, dev, stream, 20) if args.norm_reps > 0 else None
     ms_per_step = (t1 - t0) * 1e3 / args.steps
@@ -719,6 +752,8 @@ def main():
         out["add_rms_norm"] = norm
     if rope is not None:
         out["rope_cache_write"] = rope
+    if floor is not None:
+        out["small_kernel_floor"] = floor
     if chunk is not None:
         out["chunked_prefill"] = chunk
     if paged is not None:

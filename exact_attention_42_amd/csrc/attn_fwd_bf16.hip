@@ -187,17 +187,9 @@ __device__ __forceinline__ void fwd_tile_body(const FwdArgs& a) {
   // ---- epilogue: normalise, store O (bf16) and LSE (natural log) ----
   const float l_tot = xor32_sum(w.l_run);
   const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
+  store_o_group<G::DB>(a.o + ((size_t)(b * a.Hq + hq) * a.Sq + min(my_q, a.Sq - 1)) * D, w.o,
+                       inv, h, my_q < a.Sq);
   if (my_q < a.Sq) {
-    uint16_t* orow = a.o + ((size_t)(b * a.Hq + hq) * a.Sq + my_q) * D;
-#pragma unroll
-    for (int db = 0; db < G::DB; ++db)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d = 32 * db + 8 * g + 4 * h;
-        u32x2 v = {pack_bf16x2(w.o[db][4 * g + 0] * inv, w.o[db][4 * g + 1] * inv),
-                   pack_bf16x2(w.o[db][4 * g + 2] * inv, w.o[db][4 * g + 3] * inv)};
-        *reinterpret_cast<u32x2*>(orow + d) = v;
-      }
     if (a.lse != nullptr && h == 0) {
       const float lse = (l_tot > 0.f) ? (w.mref + log2_fast(l_tot)) * kLn2 : -INFINITY;
       a.lse[(size_t)(b * a.Hq + hq) * a.Sq + my_q] = lse;
@@ -447,17 +439,9 @@ __device__ __forceinline__ void fwd_pair_pipe_body(const FwdArgs& a) {
     const int my_q = qw + l32;
     const float l_tot = xor32_sum(w.l_run);
     const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
+    store_o_group<G::DB>(a.o + ((size_t)(b * a.Hq + hq) * a.Sq + min(my_q, a.Sq - 1)) * D,
+                         w.o, inv, h, my_q < a.Sq);
     if (my_q < a.Sq) {
-      uint16_t* orow = a.o + ((size_t)(b * a.Hq + hq) * a.Sq + my_q) * D;
-#pragma unroll
-      for (int db = 0; db < G::DB; ++db)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int d = 32 * db + 8 * g + 4 * h;
-          u32x2 v = {pack_bf16x2(w.o[db][4 * g + 0] * inv, w.o[db][4 * g + 1] * inv),
-                     pack_bf16x2(w.o[db][4 * g + 2] * inv, w.o[db][4 * g + 3] * inv)};
-          *reinterpret_cast<u32x2*>(orow + d) = v;
-        }
       if (a.lse != nullptr && h == 0) {
         const float lse = (l_tot > 0.f) ? (w.mref + log2_fast(l_tot)) * kLn2 : -INFINITY;
         a.lse[(size_t)(b * a.Hq + hq) * a.Sq + my_q] = lse;

@@ -264,9 +264,9 @@ __device__ __forceinline__ void fwd_paged_body(const PagedArgs& a) {
     }
 
     const float l_tot = xor32_sum(w.l_run);
-    if (my_q < Sq) {
-      const size_t row = (size_t)(qs + my_q) * a.Hq + hq;
-      if (SPLIT) {
+    const size_t row = (size_t)(qs + min(my_q, Sq - 1)) * a.Hq + hq;   // (Sq >= 1 here)
+    if (SPLIT) {
+      if (my_q < Sq) {
         // unnormalised O, reference max (base 2, scaled) and sum of this key range
         const size_t prow = (size_t)split * R + row;
         float* po = a.part_o + prow * D;
@@ -282,21 +282,12 @@ __device__ __forceinline__ void fwd_paged_body(const PagedArgs& a) {
         if (h == 0)
           *reinterpret_cast<f32x2*>(a.part_ml + prow * 2) =
               f32x2{l_tot > 0.f ? w.mref : -INFINITY, l_tot};
-      } else {
-        const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
-        uint16_t* orow = a.o + row * D;
-#pragma unroll
-        for (int db = 0; db < G::DB; ++db)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int d = 32 * db + 8 * g + 4 * h;
-            u32x2 v = {pack_bf16x2(w.o[db][4 * g + 0] * inv, w.o[db][4 * g + 1] * inv),
-                       pack_bf16x2(w.o[db][4 * g + 2] * inv, w.o[db][4 * g + 3] * inv)};
-            *reinterpret_cast<u32x2*>(orow + d) = v;
-          }
-        if (a.lse != nullptr && h == 0)
-          a.lse[row] = (l_tot > 0.f) ? (w.mref + log2_fast(l_tot)) * kLn2 : -INFINITY;
       }
+    } else {
+      const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
+      store_o_group<G::DB>(a.o + row * D, w.o, inv, h, my_q < Sq);
+      if (my_q < Sq && a.lse != nullptr && h == 0)
+        a.lse[row] = (l_tot > 0.f) ? (w.mref + log2_fast(l_tot)) * kLn2 : -INFINITY;
     }
   }
 }

@@ -629,17 +629,9 @@ __device__ __forceinline__ void fwd_wide_body(const FwdArgs& a) {
     const int my_q = qw + 32 * g + l32;
     const float l_tot = xor32_sum(w.l[g]);
     const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
+    store_o_group<G::DB>(a.o + ((size_t)(b * a.Hq + hq) * a.Sq + min(my_q, a.Sq - 1)) * D,
+                         w.o[g], inv, h, my_q < a.Sq);
     if (my_q < a.Sq) {
-      uint16_t* orow = a.o + ((size_t)(b * a.Hq + hq) * a.Sq + my_q) * D;
-#pragma unroll
-      for (int db = 0; db < G::DB; ++db)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int d = 32 * db + 8 * e + 4 * h;
-          u32x2 v = {pack_bf16x2(w.o[g][db][4 * e + 0] * inv, w.o[g][db][4 * e + 1] * inv),
-                     pack_bf16x2(w.o[g][db][4 * e + 2] * inv, w.o[g][db][4 * e + 3] * inv)};
-          *reinterpret_cast<u32x2*>(orow + d) = v;
-        }
       if (a.lse != nullptr && h == 0) {
         const float lse = (l_tot > 0.f) ? (w.m[g] + log2_fast(l_tot)) * kLn2 : -INFINITY;
         a.lse[(size_t)(b * a.Hq + hq) * a.Sq + my_q] = lse;

@@ -191,6 +191,35 @@ __device__ __forceinline__ float xor32_sum(float x) {
   return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
 }
 
+// Normalised O of one 32-query column group as bf16 into its rows. The accumulators hold O^T:
+// lane (l32, h) has element r of block db at d = 32 db + 8 (r / 4) + 4 h + r % 4 for query l32,
+// i.e. half of every 16-byte chunk of the row. Lanes l and l ^ 32 (the same query) swap halves
+// with v_permlane32_swap so that each lane holds whole chunks (the even ones on h = 0, the odd
+// ones on h = 1) and stores 16 bytes at a time: half the store instructions, and 32 contiguous
+// bytes of a row per instruction instead of 8-byte pieces. Every lane runs the swaps; only
+// lanes whose query exists (store) write.
+template <int DB>
+__device__ __forceinline__ void store_o_group(uint16_t* orow, const f32x16 (&o)[DB], float inv,
+                                              int h, bool store) {
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int e0 = 2 * k, e1 = 2 * k + 1;
+      const uint32_t x0 = pack_bf16x2(o[db][4 * e0 + 0] * inv, o[db][4 * e0 + 1] * inv);
+      const uint32_t x1 = pack_bf16x2(o[db][4 * e0 + 2] * inv, o[db][4 * e0 + 3] * inv);
+      const uint32_t y0 = pack_bf16x2(o[db][4 * e1 + 0] * inv, o[db][4 * e1 + 1] * inv);
+      const uint32_t y1 = pack_bf16x2(o[db][4 * e1 + 2] * inv, o[db][4 * e1 + 3] * inv);
+      // upper lanes of x take the lower lanes of y and vice versa: h = 0 ends with chunk e0
+      // (its own first half in x, the partner's second half in y), h = 1 with chunk e1
+      const auto s0 = __builtin_amdgcn_permlane32_swap(x0, y0, false, false);
+      const auto s1 = __builtin_amdgcn_permlane32_swap(x1, y1, false, false);
+      if (store)
+        *reinterpret_cast<u32x4*>(orow + 32 * db + 8 * (h ? e1 : e0)) =
+            u32x4{s0[0], s1[0], s0[1], s1[1]};
+    }
+}
+
 // Work item -> (batch, query head, pair). Workgroups are dispatched to the 8 XCDs round
 // robin; this gives XCD x a contiguous run of items, so the items of one KV head (adjacent
 // query heads of one batch) share that XCD's L2.

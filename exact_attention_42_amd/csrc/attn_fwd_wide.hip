@@ -376,10 +376,10 @@ __device__ __forceinline__ void wide_drain(WideWave<D>& w, WidePipe<D>& p, const
 // Work item -> (query tile rank, batch * query head). Workgroups are dispatched to the 8 XCDs
 // round robin (workgroup id mod 8), and each XCD (one L2) works through its own KV heads: when
 // the B * Hkv KV heads split evenly, XCD x takes KV heads x * n .. x * n + n - 1, in bundles of
-// ceil(8 / group) consecutive ones; within a bundle the items go tile rank by tile rank,
+// ceil(4 / group) consecutive ones; within a bundle the items go tile rank by tile rank,
 // heaviest first, each rank listing all query heads of the bundle. So the workgroups running
-// at once on an XCD read the K/V of a few KV heads through its L2, and at least 8 consecutive
-// workgroups of an XCD's queue have the same amount of work. (Within an XCD the hardware hands
+// at once on an XCD read the K/V of a few KV heads through its L2, and at least 4 consecutive
+// workgroups of an XCD's queue (one per shader engine) have the same amount of work. (Within an XCD the hardware hands
 // workgroups to its shader engines in a fixed rotation and in order: a workgroup whose engine
 // has no free CU holds back the ones behind it, so when heavy and light tiles alternate in the
 // queue, CUs wait for their next workgroup; equal neighbours avoid that.) Otherwise the items
@@ -391,7 +391,7 @@ __device__ __forceinline__ void wide_item(int id, int nitems, int ntq, int group
   if (nkv % kXcd == 0) {
     const int x = id % kXcd, j = id / kXcd;
     const int hpx = nkv / kXcd;                     // KV heads of this XCD
-    const int nb = (kXcd + group - 1) / group;      // KV heads per bundle
+    const int nb = (4 + group - 1) / group;         // KV heads per bundle
     const int per_bundle = nb * group * ntq;
     const int bundle = j / per_bundle;
     const int nbb = min(nb, hpx - bundle * nb);     // KV heads in this bundle (the last: fewer)

@@ -513,7 +513,7 @@ def decode_graph_timing(A, torch, dq, dkc, dvc, dbt, dctx, scale, reps):
     pos = (dctx - 1).to(torch.int32)
     qrot = torch.empty_like(rq)
     kc, vc = dkc.clone(), dvc.clone()
-    ws = torch.empty(A.attn_decode_workspace_bytes(B, Hq, Hkv, D, 0), dtype=torch.uint8,
+    ws = torch.empty(A.attn_decode_workspace_bytes_ex(B, Hq, Hkv, D, 0), dtype=torch.uint8,
                      device=dev)
     out = torch.empty_like(dq)
     lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
@@ -522,7 +522,7 @@ def decode_graph_timing(A, torch, dq, dkc, dvc, dbt, dctx, scale, reps):
 
     def step():
         A.rope_cache_write(rq, rk, rv, pos, kc, vc, dbt, q_out=qrot, stream=side)
-        A.attn_decode_paged_ex(qrot, kc, vc, dbt, dctx, scale=scale, out=out, lse=lse,
+        A.attn_decode_paged_full(qrot, kc, vc, dbt, dctx, scale=scale, out=out, lse=lse,
                                workspace=ws, stream=side)
 
     torch.cuda.synchronize()

@@ -18,8 +18,9 @@ __all__ = [
     "AttnError", "library_path", "load_library",
     "attn_fwd", "attn_fwd_f32", "attn_fwd_ex", "attn_fwd_workspace_bytes", "attn_fwd_force_mapping",
     "FWD_MAPPINGS", "attn_fwd_paged", "attn_fwd_paged_workspace_bytes", "attn_decode_paged",
-    "attn_decode_paged_ex", "attn_decode_paged_noalloc", "attn_decode_noalloc_max_bytes",
-    "attn_decode_workspace_bytes", "attn_decode_default_workers", "attn_status_string",
+    "attn_decode_paged_ex", "attn_decode_paged_full", "attn_decode_paged_noalloc",
+    "attn_decode_noalloc_max_bytes", "attn_decode_workspace_bytes",
+    "attn_decode_workspace_bytes_ex", "attn_decode_default_workers", "attn_status_string",
     "attn_last_error", "attn_release_workspace", "attn_abi_version", "attn_add_rms_norm",
     "add_rms_norm", "attn_rope_cache_write", "rope_cache_write", "EXPORTED_SYMBOLS",
 ]
@@ -39,12 +40,15 @@ _SIGNATURES = {
                             _I, _I, _F, _P, _Z, _P]),
     "attn_fwd_paged_workspace_bytes": (_Z, [_I, _I, _I, _I, _I, _I, _I, _I]),
     "attn_decode_paged": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P]),
-    "attn_decode_paged_ex": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I,
-                                  _I, _P, _Z, _P]),
+    "attn_decode_paged_ex": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _Z,
+                                  _P]),
+    "attn_decode_paged_full": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I,
+                                    _I, _P, _Z, _P]),
     "attn_decode_paged_noalloc": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F,
                                        _I, _I, _I, _P]),
     "attn_decode_noalloc_max_bytes": (_Z, []),
-    "attn_decode_workspace_bytes": (_Z, [_I, _I, _I, _I, _I]),
+    "attn_decode_workspace_bytes": (_Z, [_I, _I, _I]),
+    "attn_decode_workspace_bytes_ex": (_Z, [_I, _I, _I, _I, _I]),
     "attn_decode_default_workers": (_I, []),
     "attn_status_string": (ctypes.c_char_p, [_I]),
     "attn_last_error": (ctypes.c_char_p, []),
@@ -124,8 +128,12 @@ def attn_decode_default_workers() -> int:
     return load_library().attn_decode_default_workers()
 
 
-def attn_decode_workspace_bytes(B: int, Hq: int, Hkv: int, D: int, num_workers: int = 0) -> int:
-    return load_library().attn_decode_workspace_bytes(B, Hq, Hkv, D, num_workers)
+def attn_decode_workspace_bytes(B: int, Hq: int, D: int) -> int:
+    return load_library().attn_decode_workspace_bytes(B, Hq, D)
+
+
+def attn_decode_workspace_bytes_ex(B: int, Hq: int, Hkv: int, D: int, num_workers: int = 0) -> int:
+    return load_library().attn_decode_workspace_bytes_ex(B, Hq, Hkv, D, num_workers)
 
 
 def attn_release_workspace() -> None:
@@ -318,23 +326,46 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, ctx_lens, scale=None, ou
                       stream=None):
     """Paged one-token decode (bf16); returns out [B, Hq, D].
 
-    Goes through the C entry point attn_decode_paged_ex with the block table's actual row
+    Goes through the C entry point attn_decode_paged_full with the block table's actual row
     stride (``block_table.shape[1]``, which may exceed the longest context's block count, as
     in a table preallocated for the maximum context) and the pool size ``k_cache.shape[0]``,
     so a table entry outside the pool is skipped instead of read. (The 13-argument C entry
     point attn_decode_paged derives the stride from ctx_lens instead.)"""
-    o, _ = attn_decode_paged_ex(q, k_cache, v_cache, block_table, ctx_lens, scale=scale,
-                                out=out, want_lse=False, stream=stream)
+    o, _ = attn_decode_paged_full(q, k_cache, v_cache, block_table, ctx_lens, scale=scale,
+                                  out=out, want_lse=False, stream=stream)
     return o
 
 
 def attn_decode_paged_ex(q, k_cache, v_cache, block_table, ctx_lens, scale=None, out=None,
+                         workspace=None, stream=None):
+    """The C entry point attn_decode_paged_ex: the block table's row stride passed explicitly
+    (``block_table.shape[1]``) and an optional caller workspace (a uint8 device tensor of at
+    least attn_decode_workspace_bytes(B, Hq, D) bytes; None = the library's own). Block ids
+    are not range-checked; returns out [B, Hq, D]."""
+    torch = _torch()
+    B, Hq, D, nb, Hkv, bs, dev = _decode_checks(q, k_cache, v_cache, block_table, ctx_lens)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev)
+    _need(out, "out", torch.bfloat16, dev, (B, Hq, D))
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8, dev)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    with torch.cuda.device(dev):
+        _check(load_library().attn_decode_paged_ex(
+            _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(ctx_lens), _ptr(out),
+            B, Hq, Hkv, D, bs, float(scale), int(block_table.shape[1]), _ptr(workspace),
+            int(workspace.numel()) if workspace is not None else 0, _stream_ptr(dev, stream)))
+    return out
+
+
+def attn_decode_paged_full(q, k_cache, v_cache, block_table, ctx_lens, scale=None, out=None,
                          lse=None, want_lse=True, check_blocks=True, num_workers=0,
                          workspace=None, stream=None):
     """Paged decode with the explicit controls of the C ABI: returns (out, lse). The row
     stride of ``block_table`` is passed explicitly; ``check_blocks`` passes the pool size so
     out-of-range entries are skipped instead of read; ``workspace`` is an optional uint8
-    device tensor of at least attn_decode_workspace_bytes(B, Hq, Hkv, D, num_workers) bytes;
+    device tensor of at least attn_decode_workspace_bytes_ex(B, Hq, Hkv, D, num_workers) bytes;
     ``num_workers`` sets how many worker waves split the blocks (0 = the device default)."""
     torch = _torch()
     B, Hq, D, nb, Hkv, bs, dev = _decode_checks(q, k_cache, v_cache, block_table, ctx_lens)
@@ -350,7 +381,7 @@ def attn_decode_paged_ex(q, k_cache, v_cache, block_table, ctx_lens, scale=None,
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     with torch.cuda.device(dev):
-        _check(load_library().attn_decode_paged_ex(
+        _check(load_library().attn_decode_paged_full(
             _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(ctx_lens), _ptr(out),
             _ptr(lse), B, Hq, Hkv, D, bs, float(scale), int(block_table.shape[1]),
             int(nb) if check_blocks else 0, int(num_workers), _ptr(workspace),

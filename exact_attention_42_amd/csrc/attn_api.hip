@@ -430,19 +430,19 @@ int attn_rope_cache_write(const void* q, const void* k, const void* v, void* q_o
                           void* k_cache, void* v_cache, const int32_t* block_table,
                           const int32_t* positions, const int32_t* seq_ids, int T,
                           int num_seqs, int Hq, int Hkv, int D, int block_size,
-                          int table_stride, int num_blocks, float base, void* stream) {
+                          int table_stride, int num_blocks, float base, hipStream_t stream) {
   return run_rope_cache_write(q, k, v, q_out, k_cache, v_cache, block_table, positions,
                               seq_ids, T, num_seqs, Hq, Hkv, D, block_size, table_stride,
                               num_blocks, base, stream);
 }
 
 int attn_add_rms_norm(const void* x, const void* residual, const void* weight, void* out,
-                      void* residual_out, int M, int d, float eps, void* stream) {
+                      void* residual_out, int M, int d, float eps, hipStream_t stream) {
   return run_add_rms_norm(x, residual, weight, out, residual_out, M, d, eps, stream);
 }
 
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
-             int Hkv, int Sq, int Sk, int D, int causal, float scale, void* stream) {
+             int Hkv, int Sq, int Sk, int D, int causal, float scale, hipStream_t stream) {
   return run_fwd(false, q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, causal, scale, nullptr, 0,
                  stream);
 }
@@ -455,14 +455,14 @@ int attn_fwd_force_mapping(int mapping) {
 }
 
 int attn_fwd_f32(const void* q, const void* k, const void* v, void* o, float* lse, int B,
-                 int Hq, int Hkv, int Sq, int Sk, int D, int causal, float scale, void* stream) {
+                 int Hq, int Hkv, int Sq, int Sk, int D, int causal, float scale, hipStream_t stream) {
   return run_fwd(true, q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, causal, scale, nullptr, 0,
                  stream);
 }
 
 int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
                 int Hkv, int Sq, int Sk, int D, int causal, float scale, void* workspace,
-                size_t workspace_bytes, void* stream) {
+                size_t workspace_bytes, hipStream_t stream) {
   return run_fwd(false, q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, causal, scale, workspace,
                  workspace_bytes, stream);
 }
@@ -482,7 +482,7 @@ int attn_fwd_paged(const void* q, const void* k_cache, const void* v_cache,
                    const int32_t* ctx_lens, void* o, float* lse, int B, int T, int Hq, int Hkv,
                    int D, int block_size, int max_q, int max_ctx, int table_stride,
                    int num_blocks, int causal, float scale, void* workspace,
-                   size_t workspace_bytes, void* stream) {
+                   size_t workspace_bytes, hipStream_t stream) {
   return run_fwd_paged(q, k_cache, v_cache, block_table, cu_seqlens_q, ctx_lens, o, lse, B, T,
                        Hq, Hkv, D, block_size, max_q, max_ctx, table_stride, num_blocks, causal,
                        scale, workspace, workspace_bytes, stream);
@@ -502,26 +502,36 @@ size_t attn_fwd_paged_workspace_bytes(int B, int T, int Hq, int Hkv, int D, int 
 
 int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
                       const int32_t* block_table, const int32_t* ctx_lens, void* o, int B,
-                      int Hq, int Hkv, int D, int block_size, float scale, void* stream) {
+                      int Hq, int Hkv, int D, int block_size, float scale, hipStream_t stream) {
   return run_decode(q, k_cache, v_cache, block_table, ctx_lens, o, nullptr, B, Hq, Hkv, D,
                     block_size, scale, 0, 0, 0, nullptr, 0, stream);
 }
 
-int attn_decode_paged_ex(const void* q, const void* k_cache, const void* v_cache,
-                         const int32_t* block_table, const int32_t* ctx_lens, void* o,
-                         float* lse, int B, int Hq, int Hkv, int D, int block_size,
-                         float scale, int table_stride, int num_blocks, int num_workers,
-                         void* workspace, size_t workspace_bytes, void* stream) {
+int attn_decode_paged_full(const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* block_table, const int32_t* ctx_lens, void* o,
+                           float* lse, int B, int Hq, int Hkv, int D, int block_size,
+                           float scale, int table_stride, int num_blocks, int num_workers,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream) {
   return run_decode(q, k_cache, v_cache, block_table, ctx_lens, o, lse, B, Hq, Hkv, D,
                     block_size, scale, table_stride, num_blocks, num_workers, workspace,
                     workspace_bytes, stream);
+}
+
+int attn_decode_paged_ex(const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* block_table, const int32_t* ctx_lens, void* o, int B,
+                         int Hq, int Hkv, int D, int block_size, float scale,
+                         int block_table_stride, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream) {
+  return run_decode(q, k_cache, v_cache, block_table, ctx_lens, o, nullptr, B, Hq, Hkv, D,
+                    block_size, scale, block_table_stride, 0, 0, workspace, workspace_bytes,
+                    stream);
 }
 
 int attn_decode_paged_noalloc(const void* q, const void* k_cache, const void* v_cache,
                               const int32_t* block_table, const int32_t* ctx_lens, void* o,
                               float* lse, int B, int Hq, int Hkv, int D, int block_size,
                               float scale, int table_stride, int num_blocks, int num_workers,
-                              void* stream) {
+                              hipStream_t stream) {
   return run_decode(q, k_cache, v_cache, block_table, ctx_lens, o, lse, B, Hq, Hkv, D,
                     block_size, scale, table_stride, num_blocks, num_workers, nullptr, 0, stream,
                     /*use_scratch=*/true);
@@ -529,12 +539,22 @@ int attn_decode_paged_noalloc(const void* q, const void* k_cache, const void* v_
 
 size_t attn_decode_noalloc_max_bytes(void) { return kScratchBytes; }
 
-size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int D, int num_workers) {
+size_t attn_decode_workspace_bytes_ex(int B, int Hq, int Hkv, int D, int num_workers) {
   if (B < 0 || B > 65535 || Hq < 1 || Hkv < 1 || Hkv > 65535 || Hq % Hkv != 0 ||
       Hq / Hkv > 16 || (D != 64 && D != 128) || num_workers < 0 || num_workers > kMaxWorkers)
     return 0;
   return attn::decode_workspace_bytes(B, Hkv, Hq / Hkv, D,
                                       num_workers ? num_workers : default_workers());
+}
+
+size_t attn_decode_workspace_bytes(int B, int Hq, int D) {
+  // the largest need over every Hkv the decode accepts for Hq (Hkv divides Hq, Hq / Hkv <= 16)
+  size_t best = 0;
+  for (int hkv = 1; hkv <= Hq && hkv <= 65535; ++hkv) {
+    if (Hq % hkv != 0 || Hq / hkv > 16) continue;
+    best = std::max(best, attn_decode_workspace_bytes_ex(B, Hq, hkv, D, 0));
+  }
+  return best;
 }
 
 int attn_decode_default_workers(void) { return default_workers(); }
@@ -573,6 +593,6 @@ void attn_release_workspace(void) {
   if (have_cur) (void)hipSetDevice(cur);
 }
 
-int attn_abi_version(void) { return 9; }
+int attn_abi_version(void) { return 10; }
 
 }  // extern "C"

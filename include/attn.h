@@ -47,6 +47,10 @@
 #include <stddef.h>
 #include <stdint.h>
 
+/* The HIP runtime's stream handle, declared exactly as <hip/hip_runtime_api.h> declares it (an
+ * identical redeclaration, valid C11 and C++), so that this header needs no HIP include. */
+typedef struct ihipStream_t* hipStream_t;
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -75,7 +79,7 @@ enum attn_status {
  * workspace instead. */
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              int B, int Hq, int Hkv, int Sq, int Sk, int D,
-             int causal, float scale, void* stream);
+             int causal, float scale, hipStream_t stream);
 
 /* attn_fwd with a caller-owned workspace for the key-range splits: at least
  * attn_fwd_workspace_bytes(B, Hq, Hkv, Sq, Sk, D, causal) bytes, 16-byte aligned
@@ -83,7 +87,7 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  * must not overlap in time. For callers that capture graphs. */
 int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
                 int B, int Hq, int Hkv, int Sq, int Sk, int D, int causal, float scale,
-                void* workspace, size_t workspace_bytes, void* stream);
+                void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Workspace bytes attn_fwd / attn_fwd_ex need on the current device for this problem
  * (0 when it runs without key-range splits or the arguments are invalid). */
@@ -104,7 +108,7 @@ int attn_fwd_force_mapping(int mapping);
 /* The same computation with float32 q, k, v, o (full-precision path; no workspace). */
 int attn_fwd_f32(const void* q, const void* k, const void* v, void* o, float* lse,
                  int B, int Hq, int Hkv, int Sq, int Sk, int D,
-                 int causal, float scale, void* stream);
+                 int causal, float scale, hipStream_t stream);
 
 /* Prefill over a paged KV cache, for several sequences of any lengths at once (a chunked
  * prefill: the new tokens of each sequence attend to its whole cached context). Prefill and
@@ -141,7 +145,7 @@ int attn_fwd_paged(const void* q, const void* k_cache, const void* v_cache,
                    const int32_t* ctx_lens, void* o, float* lse, int B, int T, int Hq, int Hkv,
                    int D, int block_size, int max_q, int max_ctx, int table_stride,
                    int num_blocks, int causal, float scale, void* workspace,
-                   size_t workspace_bytes, void* stream);
+                   size_t workspace_bytes, hipStream_t stream);
 
 /* Workspace bytes attn_fwd_paged needs for these sizes (0 when it does not split, or for
  * invalid arguments). */
@@ -164,13 +168,27 @@ size_t attn_fwd_paged_workspace_bytes(int B, int T, int Hq, int Hkv, int D, int 
  * list into equal contiguous shares and write partial results (running max, sum and
  * unnormalised output) to the library workspace (see above), and a combine kernel merging each sequence's
  * partials with the running-softmax algebra. The caller must keep physical block ids valid;
- * they are not range-checked here (attn_decode_paged_ex can check them). */
+ * they are not range-checked here (attn_decode_paged_full can check them). */
 int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
                       const int32_t* block_table, const int32_t* ctx_lens, void* o,
                       int B, int Hq, int Hkv, int D, int block_size, float scale,
-                      void* stream);
+                      hipStream_t stream);
 
-/* attn_decode_paged with explicit controls:
+/* attn_decode_paged with an explicit block-table row stride and a caller workspace (graph
+ * capture, callers that manage their own memory):
+ *   block_table_stride: row stride of block_table in entries; <= 0 derives it as above
+ *   workspace:          caller-owned device buffer of at least
+ *                       attn_decode_workspace_bytes(B, Hq, D) bytes, 16-byte aligned; NULL =
+ *                       the library-owned workspace. Calls sharing one workspace must not
+ *                       overlap in time.
+ * Block ids are not range-checked and no LSE is written (attn_decode_paged_full has both). */
+int attn_decode_paged_ex(const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* block_table, const int32_t* ctx_lens, void* o,
+                         int B, int Hq, int Hkv, int D, int block_size, float scale,
+                         int block_table_stride, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream);
+
+/* attn_decode_paged with every control:
  *   lse:             [B, Hq] float32 log-sum-exp per head, or NULL
  *   table_stride:    row stride of block_table in entries; <= 0 derives it as above
  *   num_blocks:      size of the physical pool; > 0 makes the kernels skip (treat as empty)
@@ -179,21 +197,21 @@ int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
  *                    (attn_decode_default_workers()). Any W gives the same result up to
  *                    rounding; it only changes how the work is spread.
  *   workspace:       caller-owned device buffer of at least
- *                    attn_decode_workspace_bytes(B, Hq, Hkv, D, num_workers) bytes, 16-byte
+ *                    attn_decode_workspace_bytes_ex(B, Hq, Hkv, D, num_workers) bytes, 16-byte
  *                    aligned; NULL = use the library-owned workspace. Calls sharing one
  *                    workspace must not overlap in time. */
-int attn_decode_paged_ex(const void* q, const void* k_cache, const void* v_cache,
-                         const int32_t* block_table, const int32_t* ctx_lens, void* o,
-                         float* lse, int B, int Hq, int Hkv, int D, int block_size,
-                         float scale, int table_stride, int num_blocks, int num_workers,
-                         void* workspace, size_t workspace_bytes, void* stream);
+int attn_decode_paged_full(const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* block_table, const int32_t* ctx_lens, void* o,
+                           float* lse, int B, int Hq, int Hkv, int D, int block_size,
+                           float scale, int table_stride, int num_blocks, int num_workers,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* attn_decode_paged_ex for callers that cannot allocate device memory (code under graph
+/* attn_decode_paged_full for callers that cannot allocate device memory (code under graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): the same kernels and result,
  * but the partial results live in a fixed device array of attn_decode_noalloc_max_bytes()
  * bytes (8 MiB) inside the library, one per device, held until the process ends. The call
- * allocates and frees nothing. Arguments as for attn_decode_paged_ex, without a workspace.
- * A problem whose attn_decode_workspace_bytes(B, Hq, Hkv, D, num_workers) exceeds that size
+ * allocates and frees nothing. Arguments as for attn_decode_paged_full, without a workspace.
+ * A problem whose attn_decode_workspace_bytes_ex(B, Hq, Hkv, D, num_workers) exceeds that size
  * returns ATTN_ERR_WORKSPACE (e.g. B = 64, Hq = 32, Hkv = 8, D = 128 at the default 768
  * workers needs 2.7 MB). Nothing in the array needs clearing between calls. Every call on a
  * device shares that device's array: calls that overlap in time on one device (two streams,
@@ -202,7 +220,7 @@ int attn_decode_paged_noalloc(const void* q, const void* k_cache, const void* v_
                               const int32_t* block_table, const int32_t* ctx_lens, void* o,
                               float* lse, int B, int Hq, int Hkv, int D, int block_size,
                               float scale, int table_stride, int num_blocks, int num_workers,
-                              void* stream);
+                              hipStream_t stream);
 
 /* Size in bytes of the fixed array attn_decode_paged_noalloc uses. */
 size_t attn_decode_noalloc_max_bytes(void);
@@ -210,7 +228,12 @@ size_t attn_decode_noalloc_max_bytes(void);
 /* Bytes of workspace the decode needs (num_workers 0 = the default):
  * (W + B * Hkv) partial results of (Hq / Hkv) heads x (D + 2) floats, 16-byte padded, plus
  * 2 int32 per (sequence, KV head). 0 for invalid arguments. */
-size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int D, int num_workers);
+size_t attn_decode_workspace_bytes_ex(int B, int Hq, int Hkv, int D, int num_workers);
+
+/* Bytes of workspace attn_decode_paged_ex needs for B sequences of Hq query heads of size D,
+ * whatever Hkv (the largest attn_decode_workspace_bytes_ex(B, Hq, Hkv, D, 0) over the Hkv that
+ * divide Hq with Hq / Hkv <= 16). 0 for invalid arguments. */
+size_t attn_decode_workspace_bytes(int B, int Hq, int D);
 
 /* Default worker-wave count for the current device: 3 per compute unit. The environment
  * variable ATTN_DECODE_WORKERS = 1..65536 overrides it. */
@@ -234,7 +257,7 @@ int attn_decode_default_workers(void);
  * (ATTN_ERR_ALIGN); eps finite and >= 0 (ATTN_ERR_SCALE). One kernel on stream, no
  * synchronisation; the caller owns every buffer. */
 int attn_add_rms_norm(const void* x, const void* residual, const void* weight, void* out,
-                      void* residual_out, int M, int d, float eps, void* stream);
+                      void* residual_out, int M, int d, float eps, hipStream_t stream);
 
 /* Fused rotary position embedding + paged KV-cache store, the step before decode attention
  * ("Kernel and Operator Fusion -- Inference Optimization", §2 item 6, RoPE then KV store).
@@ -264,7 +287,7 @@ int attn_rope_cache_write(const void* q, const void* k, const void* v, void* q_o
                           void* k_cache, void* v_cache, const int32_t* block_table,
                           const int32_t* positions, const int32_t* seq_ids, int T,
                           int num_seqs, int Hq, int Hkv, int D, int block_size,
-                          int table_stride, int num_blocks, float base, void* stream);
+                          int table_stride, int num_blocks, float base, hipStream_t stream);
 
 /* Static text for a status code. */
 const char* attn_status_string(int status);
@@ -276,7 +299,7 @@ const char* attn_last_error(void);
  * that hold them). No call may be running or enqueued-and-unfinished when it is called. */
 void attn_release_workspace(void);
 
-/* ABI version of this header: 9. */
+/* ABI version of this header: 10. */
 int attn_abi_version(void);
 
 #ifdef __cplusplus

@@ -42,7 +42,7 @@ def test_status_strings_and_version():
     for code in range(9):
         assert A.attn_status_string(code) not in ("", "unknown status")
     assert A.attn_status_string(99) == "unknown status"
-    assert A.attn_abi_version() == 9
+    assert A.attn_abi_version() == 10
 
 
 def fwd(*, q=P, k=P, v=P, o=P, lse=0, B=1, Hq=32, Hkv=8, Sq=128, Sk=128, D=128, causal=1,
@@ -134,7 +134,7 @@ def dec(*, q=P, kc=P, vc=P, table=P, ctx=P, o=P, lse=0, B=64, Hq=32, Hkv=8, D=12
     lib = A.load_library()
     if not ex:
         return lib.attn_decode_paged(q, kc, vc, table, ctx, o, B, Hq, Hkv, D, bs, scale, None)
-    return lib.attn_decode_paged_ex(q, kc, vc, table, ctx, o, lse, B, Hq, Hkv, D, bs, scale,
+    return lib.attn_decode_paged_full(q, kc, vc, table, ctx, o, lse, B, Hq, Hkv, D, bs, scale,
                                     stride, nblocks, workers, ws, ws_bytes, None)
 
 
@@ -151,6 +151,38 @@ def dec(*, q=P, kc=P, vc=P, table=P, ctx=P, o=P, lse=0, B=64, Hq=32, Hkv=8, D=12
 def test_decode_rejects(kw, code):
     assert dec(**kw) == code
     assert A.attn_last_error() != ""
+
+
+def dec_contract(*, q=P, kc=P, vc=P, table=P, ctx=P, o=P, B=64, Hq=32, Hkv=8, D=128, bs=16,
+                 scale=0.08, stride=0, ws=P, ws_bytes=1 << 40):
+    return A.load_library().attn_decode_paged_ex(q, kc, vc, table, ctx, o, B, Hq, Hkv, D, bs,
+                                                 scale, stride, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), NULL), (dict(table=0), NULL), (dict(o=0), NULL), (dict(B=-1), SHAPE),
+    (dict(Hq=32, Hkv=5), SHAPE), (dict(Hq=64, Hkv=2), UNSUP), (dict(D=80), UNSUP),
+    (dict(bs=8), UNSUP), (dict(kc=P + 4), ALIGN), (dict(ctx=P + 1), ALIGN),
+    (dict(scale=NAN), SCALE), (dict(ws_bytes=100), WS), (dict(ws=P + 4), WS),
+])
+def test_decode_contract_entry_point_rejects(kw, code):
+    # the contract form of attn_decode_paged_ex: explicit stride and caller workspace only
+    assert dec_contract(**kw) == code
+    assert A.attn_last_error() != ""
+
+
+def test_decode_contract_workspace_bound():
+    # attn_decode_workspace_bytes(B, Hq, D) covers every Hkv the decode accepts for Hq
+    for B, Hq, D in [(64, 32, 128), (3, 12, 64), (1, 1, 64), (5, 48, 128), (0, 8, 64)]:
+        need = A.attn_decode_workspace_bytes(B, Hq, D)
+        ok = [h for h in range(1, Hq + 1) if Hq % h == 0 and Hq // h <= 16]
+        assert ok and need == max(A.attn_decode_workspace_bytes_ex(B, Hq, h, D, 0) for h in ok)
+    assert A.attn_decode_workspace_bytes(1, 4, 80) == 0
+    assert A.attn_decode_workspace_bytes(-1, 4, 64) == 0
+    # one byte short of the need of the Hkv that needs most is refused before any launch
+    h_max = max((h for h in range(1, 33) if 32 % h == 0 and 32 // h <= 16),
+                key=lambda h: A.attn_decode_workspace_bytes_ex(64, 32, h, 128, 0))
+    assert dec_contract(ws_bytes=A.attn_decode_workspace_bytes(64, 32, 128) - 1, Hkv=h_max) == WS
 
 
 def test_decode_plain_entry_point_rejects_before_launch():
@@ -174,15 +206,15 @@ def ws_bytes(B, Hq, Hkv, D, W):
 
 def test_decode_workspace_size():
     w = A.attn_decode_default_workers()
-    assert A.attn_decode_workspace_bytes(64, 32, 8, 128, 0) == ws_bytes(64, 32, 8, 128, w)
-    assert A.attn_decode_workspace_bytes(3, 5, 5, 64, 7) == ws_bytes(3, 5, 5, 64, 7)
-    assert A.attn_decode_workspace_bytes(3, 6, 2, 64, 1) == ws_bytes(3, 6, 2, 64, 1)
-    assert A.attn_decode_workspace_bytes(0, 32, 8, 128, 5) == ws_bytes(0, 32, 8, 128, 5)
+    assert A.attn_decode_workspace_bytes_ex(64, 32, 8, 128, 0) == ws_bytes(64, 32, 8, 128, w)
+    assert A.attn_decode_workspace_bytes_ex(3, 5, 5, 64, 7) == ws_bytes(3, 5, 5, 64, 7)
+    assert A.attn_decode_workspace_bytes_ex(3, 6, 2, 64, 1) == ws_bytes(3, 6, 2, 64, 1)
+    assert A.attn_decode_workspace_bytes_ex(0, 32, 8, 128, 5) == ws_bytes(0, 32, 8, 128, 5)
     for bad in [(1, 1, 1, 64, 65537), (1, 1, 1, 64, -1), (1, 6, 4, 64, 1), (1, 1, 1, 80, 1),
                 (-1, 1, 1, 64, 1), (1, 34, 2, 64, 1), (70000, 1, 1, 64, 1)]:
-        assert A.attn_decode_workspace_bytes(*bad) == 0, bad
+        assert A.attn_decode_workspace_bytes_ex(*bad) == 0, bad
     # one byte less than the reported size is refused before anything is launched
-    need = A.attn_decode_workspace_bytes(64, 32, 8, 128, 4)
+    need = A.attn_decode_workspace_bytes_ex(64, 32, 8, 128, 4)
     assert dec(workers=4, ws_bytes=need - 1) == WS
 
 

@@ -1,4 +1,4 @@
-"""Paged-decode parity on the GPU: attn_decode_paged / attn_decode_paged_ex (split-KV kernel +
+"""Paged-decode parity on the GPU: attn_decode_paged / attn_decode_paged_full (split-KV kernel +
 LSE-merge combine) against the fp64 oracle, plus the invariances the paged layout implies."""
 import numpy as np
 import pytest
@@ -40,6 +40,24 @@ def plain_c_decode(q, kc, vc, bt, ctx, scale):
     return o
 
 
+def test_contract_entry_point(dev):
+    """attn_decode_paged_ex in its contract form (explicit stride, caller workspace of
+    attn_decode_workspace_bytes(B, Hq, D) bytes) gives the same bits as attn_decode_paged, and
+    matches the oracle; a table wider than needed is read with its own stride."""
+    d = W.decode_inputs(B=6, Hq=8, Hkv=2, D=128, block_size=16, ctx_lo=1, ctx_hi=300, seed=41)
+    q, kc, vc, bt, ctx = upload(d, dev)
+    wide = torch.full((6, bt.shape[1] + 7), -1, dtype=torch.int32, device=dev)
+    wide[:, :bt.shape[1]] = bt
+    ws = torch.empty(A.attn_decode_workspace_bytes(6, 8, 128), dtype=torch.uint8, device=dev)
+    o = A.attn_decode_paged_ex(q, kc, vc, wide, ctx, workspace=ws)
+    o_lib = A.attn_decode_paged_ex(q, kc, vc, wide, ctx)
+    ref = A.attn_decode_paged(q, kc, vc, bt, ctx)
+    torch.cuda.synchronize()
+    assert torch.equal(o, ref) and torch.equal(o_lib, ref)
+    O, _ = oracle.decode_paged(d.q, d.k_cache, d.v_cache, d.block_table, d.ctx_lens, 16)
+    check_bf16(to_np(o), O)
+
+
 def test_config_paged_decode_b64(dev):
     """B=64, Hq=32, Hkv=8, D=128, ctx uniform in [512, 4096], 16-token blocks placed by a
     seeded permutation, tail slots poisoned with 1e4: every output element."""
@@ -47,7 +65,7 @@ def test_config_paged_decode_b64(dev):
     d = W.decode_inputs_for(cfg)
     q, kc, vc, bt, ctx = upload(d, dev)
     o = A.attn_decode_paged(q, kc, vc, bt, ctx, scale=float(cfg.scale))
-    o2, lse = A.attn_decode_paged_ex(q, kc, vc, bt, ctx, scale=float(cfg.scale))
+    o2, lse = A.attn_decode_paged_full(q, kc, vc, bt, ctx, scale=float(cfg.scale))
     o3 = plain_c_decode(q, kc, vc, bt, ctx, float(cfg.scale))
     torch.cuda.synchronize()
     assert torch.equal(o, o3)
@@ -65,7 +83,7 @@ def test_decode_edge_lengths(ctx, D, Hq, Hkv, dev):
     d = W.decode_inputs(B=len(ctx), Hq=Hq, Hkv=Hkv, D=D, block_size=16, ctx_lo=0, ctx_hi=0,
                         seed=sum(ctx) + D, ctx_lens=ctx)
     q, kc, vc, bt, cl = upload(d, dev)
-    o, lse = A.attn_decode_paged_ex(q, kc, vc, bt, cl)
+    o, lse = A.attn_decode_paged_full(q, kc, vc, bt, cl)
     torch.cuda.synchronize()
     O, L = oracle.decode_paged(d.q, d.k_cache, d.v_cache, d.block_table, d.ctx_lens, 16)
     check_bf16(to_np(o), O)
@@ -76,7 +94,7 @@ def test_decode_nan_poisoned_tails_are_never_read(dev):
     d = W.decode_inputs(B=16, Hq=32, Hkv=8, D=128, block_size=16, ctx_lo=1, ctx_hi=300,
                         seed=77, poison="nan")
     q, kc, vc, bt, cl = upload(d, dev)
-    o, lse = A.attn_decode_paged_ex(q, kc, vc, bt, cl)
+    o, lse = A.attn_decode_paged_full(q, kc, vc, bt, cl)
     torch.cuda.synchronize()
     assert bool(torch.isfinite(o).all())
     O, L = oracle.decode_paged(d.q, d.k_cache, d.v_cache, d.block_table, d.ctx_lens, 16)
@@ -87,7 +105,7 @@ def test_decode_nan_poisoned_tails_are_never_read(dev):
 def test_decode_block_permutation_is_bitwise_invariant(dev):
     d = W.decode_inputs(B=8, Hq=32, Hkv=8, D=128, block_size=16, ctx_lo=100, ctx_hi=900, seed=5)
     q, kc, vc, bt, cl = upload(d, dev)
-    o1, l1 = A.attn_decode_paged_ex(q, kc, vc, bt, cl)
+    o1, l1 = A.attn_decode_paged_full(q, kc, vc, bt, cl)
     pool = kc.shape[0]
     perm = torch.randperm(pool, generator=torch.Generator().manual_seed(3)).to(dev)
     inv = torch.empty_like(perm)
@@ -97,7 +115,7 @@ def test_decode_block_permutation_is_bitwise_invariant(dev):
     kc2[inv] = kc
     vc2[inv] = vc
     bt2 = torch.where(bt >= 0, inv[bt.clamp(min=0)].to(torch.int32), bt)
-    o2, l2 = A.attn_decode_paged_ex(q, kc2, vc2, bt2, cl)
+    o2, l2 = A.attn_decode_paged_full(q, kc2, vc2, bt2, cl)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
@@ -106,7 +124,7 @@ def test_decode_block_permutation_is_bitwise_invariant(dev):
 def test_decode_worker_count_invariance(workers, dev):
     d = W.decode_inputs(B=12, Hq=32, Hkv=8, D=128, block_size=16, ctx_lo=1, ctx_hi=2000, seed=6)
     q, kc, vc, bt, cl = upload(d, dev)
-    o, lse = A.attn_decode_paged_ex(q, kc, vc, bt, cl, num_workers=workers)
+    o, lse = A.attn_decode_paged_full(q, kc, vc, bt, cl, num_workers=workers)
     torch.cuda.synchronize()
     O, L = oracle.decode_paged(d.q, d.k_cache, d.v_cache, d.block_table, d.ctx_lens, 16)
     check_bf16(to_np(o), O)
@@ -129,7 +147,7 @@ def test_decode_matches_last_row_of_causal_prefill(dev):
         kc[perm[t // 16], :, t % 16] = k[0, :, t]
         vc[perm[t // 16], :, t % 16] = v[0, :, t]
     bt = perm[:nblk][None].copy()
-    od, ld = A.attn_decode_paged_ex(bf(q[:, :, -1]), bf(kc), bf(vc),
+    od, ld = A.attn_decode_paged_full(bf(q[:, :, -1]), bf(kc), bf(vc),
                                     torch.from_numpy(bt).to(dev),
                                     torch.tensor([n], dtype=torch.int32, device=dev))
     torch.cuda.synchronize()
@@ -143,7 +161,7 @@ def test_decode_out_of_range_blocks_are_skipped_when_checked(dev):
     q, kc, vc, bt, cl = upload(d, dev)
     bad = bt.clone()
     bad[1, 1] = 10 ** 6        # logical block 1 of sequence 1 points outside the pool
-    o, lse = A.attn_decode_paged_ex(q, kc, vc, bad, cl, check_blocks=True)
+    o, lse = A.attn_decode_paged_full(q, kc, vc, bad, cl, check_blocks=True)
     torch.cuda.synchronize()
     # sequence 1 then attends to its blocks 0 and 2 only: tokens 0-15 and 32-39
     keep = np.r_[0:16, 32:40]
@@ -160,9 +178,9 @@ def test_decode_zero_context_and_caller_workspace(dev):
     d = W.decode_inputs(B=4, Hq=8, Hkv=2, D=64, block_size=16, ctx_lo=1, ctx_hi=100, seed=9,
                         ctx_lens=[0, 50, 0, 17])
     q, kc, vc, bt, cl = upload(d, dev)
-    nbytes = A.attn_decode_workspace_bytes(4, 8, 2, 64, 4)
+    nbytes = A.attn_decode_workspace_bytes_ex(4, 8, 2, 64, 4)
     ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-    o, lse = A.attn_decode_paged_ex(q, kc, vc, bt, cl, num_workers=4, workspace=ws)
+    o, lse = A.attn_decode_paged_full(q, kc, vc, bt, cl, num_workers=4, workspace=ws)
     torch.cuda.synchronize()
     O, L = oracle.decode_paged(d.q, d.k_cache, d.v_cache, d.block_table, d.ctx_lens, 16)
     check_bf16(to_np(o), O)
@@ -173,7 +191,7 @@ def test_decode_zero_context_and_caller_workspace(dev):
 def test_decode_caller_workspace_reuse(dev):
     """One caller workspace serves calls of different shapes and worker counts in turn: each
     result equals the library-workspace call bit for bit and the oracle within the bar."""
-    ws = torch.empty(A.attn_decode_workspace_bytes(64, 32, 8, 128, 5000), dtype=torch.uint8,
+    ws = torch.empty(A.attn_decode_workspace_bytes_ex(64, 32, 8, 128, 5000), dtype=torch.uint8,
                      device=dev)
     cases = [(8, 32, 8, 128, 768), (64, 32, 8, 128, 37), (3, 8, 2, 64, 5000),
              (64, 32, 8, 128, 0), (16, 16, 1, 128, 2), (5, 8, 8, 64, 1)]
@@ -181,8 +199,8 @@ def test_decode_caller_workspace_reuse(dev):
         d = W.decode_inputs(B=B, Hq=Hq, Hkv=Hkv, D=D, block_size=16, ctx_lo=0, ctx_hi=700,
                             seed=70 + i)
         q, kc, vc, bt, cl = upload(d, dev)
-        o, lse = A.attn_decode_paged_ex(q, kc, vc, bt, cl, num_workers=wk, workspace=ws)
-        o2, lse2 = A.attn_decode_paged_ex(q, kc, vc, bt, cl, num_workers=wk)
+        o, lse = A.attn_decode_paged_full(q, kc, vc, bt, cl, num_workers=wk, workspace=ws)
+        o2, lse2 = A.attn_decode_paged_full(q, kc, vc, bt, cl, num_workers=wk)
         torch.cuda.synchronize()
         assert torch.equal(o, o2) and torch.equal(lse, lse2), f"case {i}"
         O, L = oracle.decode_paged(d.q, d.k_cache, d.v_cache, d.block_table, d.ctx_lens, 16)
@@ -206,7 +224,7 @@ def test_decode_random_shapes(seed, dev):
     d = W.decode_inputs(B=B, Hq=Hq, Hkv=Hkv, D=D, block_size=16, ctx_lo=0, ctx_hi=3000,
                         seed=1400 + seed, ctx_lens=ctx)
     q, kc, vc, bt, cl = upload(d, dev)
-    o, lse = A.attn_decode_paged_ex(q, kc, vc, bt, cl, num_workers=workers)
+    o, lse = A.attn_decode_paged_full(q, kc, vc, bt, cl, num_workers=workers)
     torch.cuda.synchronize()
     O, L = oracle.decode_paged(d.q, d.k_cache, d.v_cache, d.block_table, d.ctx_lens, 16)
     what = f"B={B} Hq={Hq} Hkv={Hkv} D={D} workers={workers}"
@@ -218,9 +236,9 @@ def test_decode_is_deterministic(dev):
     d = W.decode_inputs(B=16, Hq=32, Hkv=8, D=128, block_size=16, ctx_lo=500, ctx_hi=3000,
                         seed=10)
     q, kc, vc, bt, cl = upload(d, dev)
-    ref, ref_l = A.attn_decode_paged_ex(q, kc, vc, bt, cl)
+    ref, ref_l = A.attn_decode_paged_full(q, kc, vc, bt, cl)
     for _ in range(30):
-        o, l = A.attn_decode_paged_ex(q, kc, vc, bt, cl)
+        o, l = A.attn_decode_paged_full(q, kc, vc, bt, cl)
         assert torch.equal(o, ref) and torch.equal(l, ref_l)
 
 
@@ -270,7 +288,7 @@ def test_library_workspace_two_threads_one_stream(dev):
                         o, lse = A.attn_fwd(*fgpu, causal=True, stream=stream)
                     else:
                         (q, kc, vc, bt, cl), _, _ = probs[j]
-                        o, lse = A.attn_decode_paged_ex(q, kc, vc, bt, cl, stream=stream)
+                        o, lse = A.attn_decode_paged_full(q, kc, vc, bt, cl, stream=stream)
                     results[t].append((j, o, lse))
         except Exception as e:     # reported after the join
             errors.append(e)

@@ -131,7 +131,7 @@ def test_rope_then_decode_reads_the_store(dev):
     gkc, gvc = bf(d.k_cache, dev), bf(d.v_cache, dev)
     gbt, gcl = i32(d.block_table, dev), i32(d.ctx_lens, dev)
     qr_g = A.rope_cache_write(gq, gk, gv, i32(pos, dev), gkc, gvc, gbt)
-    o, lse = A.attn_decode_paged_ex(qr_g, gkc, gvc, gbt, gcl)
+    o, lse = A.attn_decode_paged_full(qr_g, gkc, gvc, gbt, gcl)
     torch.cuda.synchronize()
     qr, kc2, vc2 = oracle.rope_cache_write(q, k, v, pos, d.k_cache, d.v_cache, d.block_table)
     # the decode's operands are bf16 tensors: the rotated queries and the stored keys are held

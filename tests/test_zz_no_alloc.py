@@ -1,5 +1,5 @@
 """The allocation-free paged decode (attn_decode_paged_noalloc, partial results in the library's
-fixed device array) called through the C ABI, against attn_decode_paged_ex with a caller
+fixed device array) called through the C ABI, against attn_decode_paged_full with a caller
 workspace (same kernels: the results must be identical bit for bit) and against the fp64
 oracle, on two calls in a row where the second is smaller; the first call's partial results
 are still in the array when the second runs."""
@@ -37,11 +37,11 @@ def _c_noalloc(q, kc, vc, bt, ctx, o, lse, scale, workers):
 def _c_ex(q, kc, vc, bt, ctx, o, lse, scale, workers):
     B, Hq, D = q.shape
     nb, Hkv = kc.shape[0], kc.shape[1]
-    need = A.attn_decode_workspace_bytes(B, Hq, Hkv, D, workers)
+    need = A.attn_decode_workspace_bytes_ex(B, Hq, Hkv, D, workers)
     ws = torch.empty(need, dtype=torch.uint8, device=q.device)
     p = lambda t: ctypes.c_void_p(t.data_ptr())
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-    rc = A.load_library().attn_decode_paged_ex(
+    rc = A.load_library().attn_decode_paged_full(
         p(q), p(kc), p(vc), p(bt), p(ctx), p(o), p(lse), B, Hq, Hkv, D, 16, scale,
         int(bt.shape[1]), nb, workers, p(ws), need, stream)
     assert rc == 0, A.attn_last_error()
@@ -85,6 +85,6 @@ def test_noalloc_refuses_what_does_not_fit():
     d = W.decode_inputs(B=2, Hq=4, Hkv=1, D=64, block_size=16, ctx_lo=1, ctx_hi=40, seed=5)
     q, kc, vc, bt, ctx = _upload(d, dev)
     workers = 65536
-    assert A.attn_decode_workspace_bytes(2, 4, 1, 64, workers) > cap
+    assert A.attn_decode_workspace_bytes_ex(2, 4, 1, 64, workers) > cap
     with pytest.raises(A.AttnError, match="fixed scratch"):
         A.attn_decode_paged_noalloc(q, kc, vc, bt, ctx, num_workers=workers)

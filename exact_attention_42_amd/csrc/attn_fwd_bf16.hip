@@ -666,6 +666,10 @@ hipError_t launch_fwd_bf16(const FwdProblem& p, hipStream_t stream) {
   a.nsplit = p.nsplit > 1 ? p.nsplit : 1;
   a.part_o = nullptr;
   a.part_ml = nullptr;
+  // key-range splits of a problem with D = 128 and query tiles of at least the wide kernel's
+  // 256 rows run on the wide kernel: the same split count gives it half as many workgroups,
+  // one per CU where the tile kernel has two
+  if (a.nsplit > 1 && p.D == 128 && p.Sq >= kWideRows) return launch_fwd_bf16_wide(p, stream);
   if (a.nsplit > 1) {
     const size_t rows = (size_t)a.nsplit * p.B * p.Hq * p.Sq;
     a.part_o = static_cast<float*>(p.workspace);

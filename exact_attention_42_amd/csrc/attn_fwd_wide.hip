@@ -409,7 +409,10 @@ __device__ __forceinline__ void wide_item(int id, int nitems, int ntq, int group
   bh = kvh * group + (r - rank * group);
 }
 
-template <int D, bool CAUSAL>
+// SPLIT: the workgroup covers one of a.nsplit contiguous ranges of its query tile's key tiles
+// and writes its unnormalised partial result (O, reference max, sum) to the workspace; a merge
+// kernel combines the ranges (for problems with too few query tiles to fill the device).
+template <int D, bool CAUSAL, bool SPLIT>
 __device__ __forceinline__ void fwd_wide_body(const FwdArgs& a) {
   using G = Geo<D, 4>;
   // (The V stages are placed in the low 64 KiB, where a stage's base fits the 16-bit offset
@@ -432,7 +435,11 @@ __device__ __forceinline__ void fwd_wide_body(const FwdArgs& a) {
   const int h = lane >> 5;
 
   int rank, bh;
-  wide_item(blockIdx.x, a.nitems, a.ntq, a.group, a.B * a.Hkv, rank, bh);
+  wide_item(blockIdx.x, a.nitems, SPLIT ? a.ntq * a.nsplit : a.ntq, a.group, a.B * a.Hkv, rank,
+            bh);
+  // (with splits, the ranges of one query tile are neighbours in the order, equal in work)
+  const int split = SPLIT ? rank % a.nsplit : 0;
+  if (SPLIT) rank /= a.nsplit;
   const int tile = CAUSAL ? (a.ntq - 1 - rank) : rank;
   const int b = bh / a.Hq;
   const int hq = bh - b * a.Hq;
@@ -449,7 +456,12 @@ __device__ __forceinline__ void fwd_wide_body(const FwdArgs& a) {
   const int qend = min(q0 + kWideBM, a.Sq);         // rows of the workgroup end here
   int kend = a.Sk;
   if (CAUSAL) kend = min(a.Sk, max(0, qend + off));
-  const int nt = (kend + kBN - 1) / kBN;            // key tiles the workgroup loads
+  const int nt_all = (kend + kBN - 1) / kBN;        // key tiles the query tile sees
+  // this workgroup's key tiles t0 .. t0 + nt - 1 (all of them without splits); below, tile and
+  // block indices count from t0, and kt0 is the first key
+  const int t0 = SPLIT ? split * nt_all / a.nsplit : 0;
+  const int nt = SPLIT ? (split + 1) * nt_all / a.nsplit - t0 : nt_all;
+  const int kt0 = t0 * kBN;
   int nblk = 0;                                     // 32-key blocks this wave scores
   int nunm = 0;                                     // leading blocks needing no mask
   if (qw < a.Sq) {
@@ -461,6 +473,10 @@ __device__ __forceinline__ void fwd_wide_body(const FwdArgs& a) {
     if (CAUSAL) nunm = min(nunm, max(0, qw + off + 1) / 32);
     // (rows past Sq see every key of the tile: they need no mask, and are never stored)
     nunm = min(nunm, nblk);
+    if (SPLIT) {
+      nblk = max(0, min(nblk, 2 * (t0 + nt)) - 2 * t0);
+      nunm = min(max(0, nunm - 2 * t0), nblk);
+    }
   }
 
   WideWave<D> w;
@@ -527,7 +543,8 @@ __device__ __forceinline__ void fwd_wide_body(const FwdArgs& a) {
 #pragma unroll
   for (int t = 0; t < 3; ++t) {
 #pragma unroll
-    for (int j = 0; j < (t < 2 ? kParts : 3); ++j) dma.issue_part_unclamped(KS[t], VS[t], t * kBN, j);
+    for (int j = 0; j < (t < 2 ? kParts : 3); ++j)
+      dma.issue_part_unclamped(KS[t], VS[t], kt0 + t * kBN, j);
   }
   __builtin_amdgcn_s_waitcnt(kWaitVm11);
   __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
@@ -567,8 +584,8 @@ __device__ __forceinline__ void fwd_wide_body(const FwdArgs& a) {
     char* const v2 = VS[(ST + 2) % kStages];
     char* const k3 = KS[(ST + 3) % kStages];               // tile T + 3 (loads 0..2 now)
     char* const v3 = VS[(ST + 3) % kStages];
-    const int k0 = T * kBN;
-    const int kt2 = load_tile(T + 2) * kBN, kt3 = load_tile(T + 3) * kBN;
+    const int k0 = kt0 + T * kBN;
+    const int kt2 = kt0 + load_tile(T + 2) * kBN, kt3 = kt0 + load_tile(T + 3) * kBN;
     // loads 3..7 of tile T + 2 spread over block 2T (stretches 1a, 1a, 2a, 2a, 2b), loads 0..2
     // of tile T + 3 over the stretches of block 2T + 1 after its barrier (2a, 2b, 2b)
     auto hook0 = [&](int st, int slot) {
@@ -623,6 +640,31 @@ __device__ __forceinline__ void fwd_wide_body(const FwdArgs& a) {
   }
   __builtin_amdgcn_s_waitcnt(kWaitVm0);   // (no load may still be writing LDS at the end)
 
+  if (SPLIT) {
+    // ---- partial result: unnormalised O, reference max (base 2, scaled) and sum ----
+    const size_t nrows = (size_t)a.B * a.Hq * a.Sq;
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const int my_q = qw + 32 * g + l32;
+      const float l_tot = xor32_sum(w.l[g]);
+      if (my_q < a.Sq) {
+        const size_t prow = (size_t)split * nrows + (size_t)(b * a.Hq + hq) * a.Sq + my_q;
+        float* po = a.part_o + prow * D;
+#pragma unroll
+        for (int db = 0; db < G::DB; ++db)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            *reinterpret_cast<f32x4*>(po + 32 * db + 8 * e + 4 * h) =
+                f32x4{w.o[g][db][4 * e + 0], w.o[g][db][4 * e + 1], w.o[g][db][4 * e + 2],
+                      w.o[g][db][4 * e + 3]};
+        if (h == 0)
+          *reinterpret_cast<f32x2*>(a.part_ml + prow * 2) =
+              f32x2{l_tot > 0.f ? w.m[g] : -INFINITY, l_tot};
+      }
+    }
+    return;
+  }
+
   // ---- epilogue: normalise, store O (bf16) and LSE (natural log) ----
 #pragma unroll
   for (int g = 0; g < 2; ++g) {
@@ -641,9 +683,16 @@ __device__ __forceinline__ void fwd_wide_body(const FwdArgs& a) {
 }
 
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void fwd_bf16_d128_causal_wide(FwdArgs a) { fwd_wide_body<128, true>(a); }
+void fwd_bf16_d128_causal_wide(FwdArgs a) { fwd_wide_body<128, true, false>(a); }
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void fwd_bf16_d128_wide(FwdArgs a) { fwd_wide_body<128, false>(a); }
+void fwd_bf16_d128_wide(FwdArgs a) { fwd_wide_body<128, false, false>(a); }
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void fwd_bf16_d128_causal_wide_split(FwdArgs a) { fwd_wide_body<128, true, true>(a); }
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void fwd_bf16_d128_wide_split(FwdArgs a) { fwd_wide_body<128, false, true>(a); }
+__global__ __launch_bounds__(256) void fwd_bf16_d128_wide_split_combine(FwdArgs a) {
+  fwd_split_combine_body<128>(a);
+}
 
 }  // namespace
 
@@ -660,11 +709,25 @@ hipError_t launch_fwd_bf16_wide(const FwdProblem& p, hipStream_t stream) {
   float c = p.scale * kLog2e;
   if (!(c > 0.f)) c = 1.17549435e-38f;   // scale 0: uniform weights, -inf * c stays -inf
   a.c = c;
-  a.nsplit = 1;
-  const long long nwg = (long long)a.ntq * p.B * p.Hq;
+  a.nsplit = p.nsplit > 1 ? p.nsplit : 1;
+  const long long nwg = (long long)a.ntq * a.nsplit * p.B * p.Hq;
   if (nwg == 0) return hipSuccess;
   if (nwg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   a.nitems = (int)nwg;
+  if (a.nsplit > 1) {
+    // the key ranges of each query tile, then their merge (workspace as for the other forward
+    // kernels' splits: fwd_bf16_workspace_bytes)
+    const size_t nrows = (size_t)p.B * p.Hq * p.Sq;
+    a.part_o = static_cast<float*>(p.workspace);
+    a.part_ml = a.part_o + (size_t)a.nsplit * nrows * p.D;
+    dim3 grid((unsigned)nwg), block(256);
+    if (p.causal) hipLaunchKernelGGL(fwd_bf16_d128_causal_wide_split, grid, block, 0, stream, a);
+    else hipLaunchKernelGGL(fwd_bf16_d128_wide_split, grid, block, 0, stream, a);
+    const int rows_per_block = 256 / (p.D / 4);
+    dim3 cgrid((unsigned)((nrows + rows_per_block - 1) / rows_per_block)), cblock(256);
+    hipLaunchKernelGGL(fwd_bf16_d128_wide_split_combine, cgrid, cblock, 0, stream, a);
+    return hipGetLastError();
+  }
   dim3 grid((unsigned)nwg), block(256);
   if (p.causal) hipLaunchKernelGGL(fwd_bf16_d128_causal_wide, grid, block, 0, stream, a);
   else hipLaunchKernelGGL(fwd_bf16_d128_wide, grid, block, 0, stream, a);

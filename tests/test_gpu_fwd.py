@@ -364,6 +364,26 @@ def test_key_split_and_whole_paths(B, Hq, Hkv, Sq, Sk, causal, dev):
     check_lse(lse, L)
 
 
+@pytest.mark.parametrize("B,Hq,Hkv,Sq,Sk,causal", [
+    (1, 2, 1, 257, 3001, True),    # a ragged query tile and a partial last key tile
+    (1, 2, 2, 513, 2050, False),
+    (2, 4, 1, 256, 1000, True),    # 4 query heads per KV head
+    (1, 8, 2, 1000, 6000, True),   # eight ranges per query tile
+    (1, 3, 3, 600, 600, True),     # Sq = Sk: the last range holds the diagonal
+])
+def test_wide_key_splits(B, Hq, Hkv, Sq, Sk, causal, dev):
+    """Few 256-row query tiles with D = 128: the wide kernel takes the key ranges (one per
+    workgroup) and a second kernel merges them; every element against the oracle."""
+    assert A.attn_fwd_workspace_bytes(B, Hq, Hkv, Sq, Sk, 128, causal) > 0   # (splits)
+    q, k, v = W.fwd_inputs(B, Hq, Hkv, Sq, Sk, 128, seed=B * 7 + Sq * 3 + Sk)
+    scale = np.float32(1 / np.sqrt(128))
+    o, lse = run_bf16(q, k, v, causal, scale, dev)
+    O, L = oracle.attention(q, k, v, causal=causal, scale=scale)
+    what = f"B={B} Hq={Hq} Hkv={Hkv} Sq={Sq} Sk={Sk} causal={causal}"
+    check_bf16(o, O, what=what + " O")
+    check_lse(lse, L, what=what + " LSE")
+
+
 # ---- the wide kernel (one wave per SIMD, 256-row workgroups) ----
 
 @pytest.fixture

@@ -146,18 +146,20 @@ def test_paged_prefill_workloads(dev, name):
 
 
 def test_paged_chunk_equals_contiguous_chunk(dev):
-    """The 512-token chunk over 4096 keys through the paged cache and through the contiguous
-    forward (same keys gathered into [B, Hkv, S, D]) run the same tile arithmetic with the same
-    key ranges, so they agree bit for bit."""
-    cfg = W.PAGED_PREFILL_CONFIGS["paged_prefill_512_of_4096"]
-    x = W.paged_prefill_inputs_for(cfg)
-    o, lse = run(x, dev, True, cfg.scale)
+    """A 512-token chunk over 4096 keys with D = 64 through the paged cache and through the
+    contiguous forward (same keys gathered into [B, Hkv, S, D]): both run the tile kernel's
+    arithmetic with the same key ranges, so they agree bit for bit. (With D = 128 the contiguous
+    forward takes such a chunk on the wide kernel instead, which rounds in another order.)"""
+    x = W.paged_prefill_inputs(32, 8, 64, (512,), (4096,), seed=1012)
+    scale = np.float32(1 / np.sqrt(64))
+    o, lse = run(x, dev, True, scale)
     K = oracle.gather_paged(x.k_cache, x.block_table, 4096, 0, 16)[None]
     V = oracle.gather_paged(x.v_cache, x.block_table, 4096, 0, 16)[None]
     bf = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev).to(
         torch.bfloat16)
     qd = bf(np.transpose(x.q, (1, 0, 2))[None])
-    od, ld = A.attn_fwd(qd, bf(K), bf(V), causal=True, scale=float(cfg.scale))
+    od, ld = A.attn_fwd(qd, bf(K), bf(V), causal=True, scale=float(scale))
     torch.cuda.synchronize()
     assert torch.equal(o, od[0].transpose(0, 1).contiguous())
     assert torch.equal(lse, ld[0].transpose(0, 1).contiguous())
+    check(x, o, lse, True, scale, what="paged D=64 chunk")

@@ -384,6 +384,26 @@ def test_wide_key_splits(B, Hq, Hkv, Sq, Sk, causal, dev):
     check_lse(lse, L, what=what + " LSE")
 
 
+@pytest.mark.parametrize("seed", range(6))
+def test_wide_key_splits_random(seed, dev):
+    """Random few-tile shapes with D = 128 and Sq >= 256 (the wide kernel's key-range splits):
+    ragged query and key ends, Sq above and below Sk, both masks, GQA."""
+    rng = np.random.default_rng(900 + seed)
+    Hkv = int(rng.integers(1, 3))
+    Hq = Hkv * int(rng.choice([1, 2, 4]))
+    Sq = int(rng.integers(256, 900))
+    Sk = int(rng.integers(1000, 5000))     # (at least 16 key tiles: always split)
+    causal = bool(rng.integers(0, 2))
+    assert A.attn_fwd_workspace_bytes(1, Hq, Hkv, Sq, Sk, 128, causal) > 0
+    q, k, v = W.fwd_inputs(1, Hq, Hkv, Sq, Sk, 128, seed=950 + seed)
+    scale = np.float32(1 / np.sqrt(128))
+    o, lse = run_bf16(q, k, v, causal, scale, dev)
+    O, L = oracle.attention(q, k, v, causal=causal, scale=scale)
+    what = f"Hq={Hq} Hkv={Hkv} Sq={Sq} Sk={Sk} causal={causal}"
+    check_bf16(o, O, what=what + " O")
+    check_lse(lse, L, what=what + " LSE")
+
+
 # ---- the wide kernel (one wave per SIMD, 256-row workgroups) ----
 
 @pytest.fixture

@@ -136,6 +136,30 @@ def test_paged_prefill_rows_outside_sequences_untouched(dev):
     check(x, o[:T], lse[:T], True, np.float32(1 / 8), what="padded q")
 
 
+def random_paged_case(seed):
+    """1-6 sequences with random chunk lengths (0-700) over random contexts (the chunk's
+    length up to 3000 more), random GQA group and head size, either mask."""
+    rng = np.random.default_rng(4000 + seed)
+    nseq = int(rng.integers(1, 7))
+    Hkv = int(rng.choice([1, 2, 4]))
+    Hq = Hkv * int(rng.choice([1, 2, 4]))
+    D = int(rng.choice([64, 128]))
+    ql = [int(x) for x in rng.integers(0, 700, nseq)]
+    kl = [q + int(rng.integers(0, 3000)) for q in ql]
+    return Hq, Hkv, D, tuple(ql), tuple(kl), bool(rng.integers(0, 2))
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_paged_prefill_random_batches(dev, seed):
+    Hq, Hkv, D, ql, kl, causal = random_paged_case(seed)
+    x = W.paged_prefill_inputs(Hq, Hkv, D, ql, kl, seed=4100 + seed, poison="nan",
+                               extra_blocks=int(seed))
+    scale = np.float32(1 / np.sqrt(D))
+    o, lse = run(x, dev, causal, scale, max_q=max(1, max(ql)), max_ctx=max(kl))
+    check(x, o, lse, causal, scale, what=f"random batch {seed}: Hq={Hq} Hkv={Hkv} D={D} "
+          f"q={ql} k={kl} causal={causal}")
+
+
 @pytest.mark.parametrize("name", list(W.PAGED_PREFILL_CONFIGS))
 def test_paged_prefill_workloads(dev, name):
     """The bench's paged-prefill workloads at full size, every element against the oracle."""

@@ -461,6 +461,66 @@ def test_fwd_wide_random_shapes(seed, dev, forced_wide):
     check_lse(lse, L, what=what + " LSE")
 
 
+# More 256-row items than compute units, with Sk a whole number of 64-key tiles: one workgroup
+# per CU walks several items in turn (B, Hq, Hkv, Sq, Sk, causal). Two or more rounds, the last
+# partial; both masks; queries ending before and after the keys (the first items of the last
+# case see no key at all); a ragged last query tile; KV heads that split evenly over the 8 XCDs
+# and ones that do not (12).
+WIDE_PERSISTENT = [
+    (2, 48, 8, 768, 768, True), (3, 48, 8, 640, 1088, False), (1, 60, 12, 1280, 1280, True),
+    (2, 72, 8, 512, 1216, True), (1, 96, 16, 900, 640, True),
+]
+
+
+@pytest.mark.parametrize("shape", WIDE_PERSISTENT, ids=lambda s: "x".join(map(str, s)))
+def test_fwd_wide_persistent(shape, dev, forced_wide):
+    B, Hq, Hkv, Sq, Sk, causal = shape
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert ((Sq + 255) // 256) * B * Hq > cus and Sk % 64 == 0
+    q, k, v = W.fwd_inputs(B, Hq, Hkv, Sq, Sk, 128, seed=7700 + Sq + Sk + Hq)
+    scale = np.float32(1 / np.sqrt(128))
+    o, lse = run_bf16(q, k, v, causal, scale, dev)
+    O, L = oracle.attention(q, k, v, causal=causal, scale=scale)
+    check_bf16(o, O, what=f"{shape} O")
+    check_lse(lse, L, what=f"{shape} LSE")
+
+
+def test_fwd_wide_persistent_is_deterministic(dev, forced_wide):
+    """Workgroups that walk several items give identical bits on repeated launches, and the
+    same bits as a problem of one item per workgroup would for the same rows (the batch entry
+    alone, 144 items)."""
+    q, k, v = W.fwd_inputs(2, 48, 8, 768, 768, 128, seed=21)
+    qg, kg, vg = (_gpu(x, dev, torch.bfloat16) for x in (q, k, v))
+    ref, ref_l = A.attn_fwd(qg, kg, vg, causal=True)
+    for _ in range(10):
+        o, l = A.attn_fwd(qg, kg, vg, causal=True)
+        assert torch.equal(o, ref) and torch.equal(l, ref_l)
+    o1, l1 = A.attn_fwd(qg[1:].contiguous(), kg[1:].contiguous(), vg[1:].contiguous(),
+                        causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1[0], ref[1]) and torch.equal(l1[0], ref_l[1])
+
+
+def test_fwd_wide_persistent_two_streams(dev, forced_wide):
+    """The same many-item problem launched alternately on two streams without synchronising
+    between them: each stream claims items through its own counters, and every launch gives the
+    bits of a launch alone."""
+    q, k, v = W.fwd_inputs(1, 60, 12, 1280, 1280, 128, seed=22)
+    qg, kg, vg = (_gpu(x, dev, torch.bfloat16) for x in (q, k, v))
+    ref, ref_l = A.attn_fwd(qg, kg, vg, causal=True)
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+    outs = []
+    for i in range(6):
+        with torch.cuda.stream(streams[i % 2]):
+            outs.append(A.attn_fwd(qg, kg, vg, causal=True))
+    torch.cuda.synchronize()
+    for o, l in outs:
+        assert torch.equal(o, ref) and torch.equal(l, ref_l)
+
+
 def test_fwd_wide_is_deterministic(dev, forced_wide):
     """Repeated launches give identical bits (the four LDS stages and the spread loads leave no
     race)."""

@@ -182,42 +182,6 @@ int get_workspace_locked(void* stream, size_t need, void** out) {
   return ATTN_OK;
 }
 
-// Claim counters of the bf16 wide kernel for (current device, stream): allocated and cleared
-// once, never freed (every launch leaves them cleared). None on a stream being captured (the
-// graph may be replayed on another stream, where two replays would share them) or on the
-// per-thread default stream (one handle for many streams): the kernel then assigns its items
-// statically. Launches on one stream run one after another, so they never share counters.
-std::mutex g_sched_mutex;
-std::map<std::pair<int, void*>, int*> g_sched;
-
-int* sched_block(void* stream) {
-  if (static_cast<hipStream_t>(stream) == hipStreamPerThread) return nullptr;
-  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-  int dev = 0;
-  if (hipStreamIsCapturing(static_cast<hipStream_t>(stream), &cap) != hipSuccess ||
-      cap != hipStreamCaptureStatusNone || hipGetDevice(&dev) != hipSuccess) {
-    (void)hipGetLastError();
-    return nullptr;
-  }
-  std::lock_guard<std::mutex> lock(g_sched_mutex);
-  int*& blk = g_sched[{dev, stream}];
-  if (blk == nullptr) {
-    const size_t bytes = attn::kSchedInts * sizeof(int);
-    void* ptr = nullptr;
-    if (hipMalloc(&ptr, bytes) != hipSuccess) {
-      (void)hipGetLastError();
-      return nullptr;
-    }
-    if (hipMemsetAsync(ptr, 0, bytes, static_cast<hipStream_t>(stream)) != hipSuccess) {
-      (void)hipGetLastError();
-      (void)hipFree(ptr);
-      return nullptr;
-    }
-    blk = static_cast<int*>(ptr);
-  }
-  return blk;
-}
-
 // Device address of `scratch` on the current device, looked up once per device (with that
 // device current) and kept; a fixed table, so the lookup allocates nothing either.
 constexpr int kMaxDevices = 64;
@@ -276,7 +240,6 @@ int run_fwd(bool f32, const void* q, const void* k, const void* v, void* o, floa
       }
     }
   }
-  if (!f32 && p.nsplit <= 1) p.sched = sched_block(stream);
   hipError_t e = f32 ? attn::launch_fwd_f32(p, static_cast<hipStream_t>(stream))
                      : attn::launch_fwd_bf16(p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, f32 ? "attn_fwd_f32 launch" : "attn_fwd launch");

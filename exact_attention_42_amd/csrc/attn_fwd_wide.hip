@@ -385,37 +385,19 @@ __device__ __forceinline__ void wide_drain(WideWave<D>& w, WidePipe<D>& p, const
 // queue, CUs wait for their next workgroup; equal neighbours avoid that.) Otherwise the items
 // are ordered KV head by KV head (heaviest tile first, the query heads of a tile together) and
 // XCD x takes a contiguous eighth of that order.
-//
-// Phased (no key-range splits): an XCD's order takes the tile ranks in four ranges, heaviest
-// range first, and each range bundle by bundle. The last items of every XCD are then the
-// lightest quarter, which workgroups that run out of work share out at the end; each range
-// still reads one bundle's K/V at a time (a bundle's K/V prefix is read up to four times).
 __device__ __forceinline__ void wide_item(int id, int nitems, int ntq, int group, int nkv,
-                                          bool phased, int& rank, int& bh) {
+                                          int& rank, int& bh) {
   constexpr int kXcd = 8;
   if (nkv % kXcd == 0) {
-    const int x = id % kXcd;
-    int j = id / kXcd;
+    const int x = id % kXcd, j = id / kXcd;
     const int hpx = nkv / kXcd;                     // KV heads of this XCD
     const int nb = (4 + group - 1) / group;         // KV heads per bundle
-    int r0 = 0, nr = ntq;                           // tile ranks r0 .. r0 + nr - 1
-    if (phased) {
-      const int nph = min(4, ntq);
-      for (int ph = 0; ph < nph; ++ph) {
-        const int lo = ph * ntq / nph, hi = (ph + 1) * ntq / nph;
-        const int cnt = hpx * group * (hi - lo);   // items of this range
-        r0 = lo;
-        nr = hi - lo;
-        if (j < cnt) break;
-        j -= cnt;
-      }
-    }
-    const int per_bundle = nb * group * nr;
+    const int per_bundle = nb * group * ntq;
     const int bundle = j / per_bundle;
     const int nbb = min(nb, hpx - bundle * nb);     // KV heads in this bundle (the last: fewer)
     const int r = j - bundle * per_bundle;
-    rank = r0 + r / (nbb * group);
-    const int rem = r % (nbb * group);              // (KV head in bundle) * group + g
+    rank = r / (nbb * group);
+    const int rem = r - rank * (nbb * group);       // (KV head in bundle) * group + g
     bh = (x * hpx + bundle * nb) * group + rem;     // (b * Hkv + hk) * group + g = b * Hq + hq
     return;
   }
@@ -446,12 +428,88 @@ __device__ __forceinline__ void fwd_wide_body(const FwdArgs& a) {
   char* const KS[kStages] = {b_k0, b_k1, b_k2, b_k3};
   char* const VS[kStages] = {a_v0, a_v1, a_v2, a_v3};
 
-  const int tid0 = threadIdx.x;
-  const int wave = wave_uniform(tid0 >> 6);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = wave_uniform(tid >> 6);
+  const int l32 = lane & 31;
+  const int h = lane >> 5;
+
+  int rank, bh;
+  wide_item(blockIdx.x, a.nitems, SPLIT ? a.ntq * a.nsplit : a.ntq, a.group, a.B * a.Hkv, rank,
+            bh);
+  // (with splits, the ranges of one query tile are neighbours in the order, equal in work)
+  const int split = SPLIT ? rank % a.nsplit : 0;
+  if (SPLIT) rank /= a.nsplit;
+  const int tile = CAUSAL ? (a.ntq - 1 - rank) : rank;
+  const int b = bh / a.Hq;
+  const int hq = bh - b * a.Hq;
+  const int hk = hq / a.group;
+  const int q0 = tile * kWideBM;
+  const int qw = q0 + wave * kWideRows;
+  const int off = a.Sk - a.Sq;
+
+  const uint16_t* qbase = a.q + ((size_t)(b * a.Hq + hq) * a.Sq) * D;
+  const uint16_t* kbase = a.k + ((size_t)(b * a.Hkv + hk) * a.Sk) * D;
+  const uint16_t* vbase = a.v + ((size_t)(b * a.Hkv + hk) * a.Sk) * D;
+
+  // ---- key tiles of the workgroup, and blocks of this wave ----
+  const int qend = min(q0 + kWideBM, a.Sq);         // rows of the workgroup end here
+  int kend = a.Sk;
+  if (CAUSAL) kend = min(a.Sk, max(0, qend + off));
+  const int nt_all = (kend + kBN - 1) / kBN;        // key tiles the query tile sees
+  // this workgroup's key tiles t0 .. t0 + nt - 1 (all of them without splits); below, tile and
+  // block indices count from t0, and kt0 is the first key
+  const int t0 = SPLIT ? split * nt_all / a.nsplit : 0;
+  const int nt = SPLIT ? (split + 1) * nt_all / a.nsplit - t0 : nt_all;
+  const int kt0 = t0 * kBN;
+  int nblk = 0;                                     // 32-key blocks this wave scores
+  int nunm = 0;                                     // leading blocks needing no mask
+  if (qw < a.Sq) {
+    const int qlast = min(qw + kWideRows, a.Sq) - 1;
+    int kw = a.Sk;
+    if (CAUSAL) kw = min(a.Sk, max(0, qlast + off + 1));
+    nblk = (kw + 31) / 32;
+    nunm = a.Sk / 32;
+    if (CAUSAL) nunm = min(nunm, max(0, qw + off + 1) / 32);
+    // (rows past Sq see every key of the tile: they need no mask, and are never stored)
+    nunm = min(nunm, nblk);
+    if (SPLIT) {
+      nblk = max(0, min(nblk, 2 * (t0 + nt)) - 2 * t0);
+      nunm = min(max(0, nunm - 2 * t0), nblk);
+    }
+  }
 
   WideWave<D> w;
+  const float a_inv_c = 1.f / a.c;
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    const int qi = qw + 32 * g + l32;
+#pragma unroll
+    for (int kk = 0; kk < G::KS; ++kk) {
+      if (qi < a.Sq)
+        w.qf[g][kk] = *reinterpret_cast<const u32x4*>(qbase + (size_t)qi * D + kk * 16 + h * 8);
+      else
+        w.qf[g][kk] = u32x4{0, 0, 0, 0};
+    }
+    w.lim[g] = CAUSAL ? min(a.Sk, qi + off + 1) : a.Sk;
+#pragma unroll
+    for (int i = 0; i < G::DB; ++i) w.o[g][i] = f32x16{};
+    w.m[g] = kNoRef;
+    w.l[g] = 0.f;
+    w.thr[g] = (kNoRef + kLazy) * a_inv_c;
+  }
+#pragma unroll
+  for (int kk = 0; kk < G::KS; ++kk)
+    w.koff[kk] = l32 * G::kRow + (((2 * kk + h) ^ kswz<D>(l32)) * 16);
+  {
+    const int g = lane >> 4, j = lane & 15;
+    const int keyl = 4 * (g >> 1) + (j >> 2);
+    const int small = 2 * (g & 1) + ((j & 3) >> 1);
+#pragma unroll
+    for (int db = 0; db < G::DB; ++db)
+      w.voff[db] = keyl * G::kRow + (((4 * db + small) ^ vswz<D>(keyl)) * 16) + 8 * (j & 1);
+  }
   const float c = a.c;
-  const float a_inv_c = 1.f / c;
 
   // Every stage starts cleared: the dummy block before the first reads "V" from the second half
   // of the last stage (0 * V must stay 0), and rows past Sk of a partial last tile are loaded
@@ -463,364 +521,163 @@ __device__ __forceinline__ void fwd_wide_body(const FwdArgs& a) {
       u32x4* vz = reinterpret_cast<u32x4*>(VS[st]);
 #pragma unroll
       for (int i = 0; i < G::kTile / 16 / 256; ++i) {
-        kz[i * 256 + tid0] = u32x4{0, 0, 0, 0};
-        vz[i * 256 + tid0] = u32x4{0, 0, 0, 0};
+        kz[i * 256 + tid] = u32x4{0, 0, 0, 0};
+        vz[i * 256 + tid] = u32x4{0, 0, 0, 0};
       }
     }
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   }
+  TileDma<D, 4> dma;
+  dma.init(wave, lane, kbase, vbase, a.Sk);
+  // Loads: a wave's 8 loads of tile X go out one at a time between the matrix-core instructions
+  // of iterations 2X - 5 (after its barrier: loads 0..2) and 2X - 4 (loads 3..7), into the stage
+  // of tile X - 4, which no wave reads after barrier X - 3. Every load is issued, so the count of
+  // loads in flight after tile T + 1's is always 8 at barrier T: a tile past the workgroup's
+  // last loads, instead, the tile its stage already holds (X - 4, the same bytes), or for X < 4
+  // tile X itself into a stage no tile uses. Tiles 0 and 1 and the first three loads of tile 2
+  // are issued here; then wait for tile 0 (and the Q fragments, loaded earlier).
+  constexpr int kParts = 2 * G::kIPW;      // loads per wave and tile
+  static_assert(kParts == 8, "D = 128: 4 K and 4 V loads per wave and tile");
+#pragma unroll
+  for (int t = 0; t < 3; ++t) {
+#pragma unroll
+    for (int j = 0; j < (t < 2 ? kParts : 3); ++j)
+      dma.issue_part_unclamped(KS[t], VS[t], kt0 + t * kBN, j);
+  }
+  __builtin_amdgcn_s_waitcnt(kWaitVm11);
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 
-  // Items. With fewer workgroups than items (one per CU, launched only when Sk is a whole number
-  // of key tiles, so no item reads another's bytes under a mask), each workgroup walks several.
-  // The items of XCD x are x + 8 * position, positions in the order wide_item gives (heaviest
-  // first within each bundle of KV heads); workgroup s of XCD x starts with position s (S
-  // workgroups per XCD). With claim counters (a.sched), each next item is claimed one item
-  // ahead: the front of the own XCD's remaining positions, and once those are gone, the back
-  // (the lightest items) of another XCD's. The XCDs run at different clocks (a few percent
-  // apart under this load), and taking each other's last items evens out their finishing times.
-  // One 64-bit word per XCD counts both ends (front claims in the low half, back claims in the
-  // high half), so each claim sees both counts at once and every position is claimed once.
-  // Without counters, workgroup s takes positions s, 2S-1-s, 2S+s, ... (rounds of equal or
-  // decreasing work per item, so pairs of rounds even out).
-  const bool persist = !SPLIT && (int)gridDim.x < a.nitems;
-  const bool dyn = persist && a.sched != nullptr;
-  const int xs = blockIdx.x & 7, slot = blockIdx.x >> 3, nslot = gridDim.x >> 3;
-  auto round_item = [&](int r) {
-    return xs + 8 * (r * nslot + ((r & 1) ? nslot - 1 - slot : slot));
+  // the dummy block before the first (slot 1, read by block 0): scores -inf, P^T zero
+  WidePipe<D> p;
+  if (nblk > 0) read_k<D>(w, KS[0], p.kf);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) p.s1[1][r] = -INFINITY;
+  p.mu1[1] = kNoRef;
+  p.p0[1][0] = u32x4{0, 0, 0, 0};
+  p.p0[1][1] = u32x4{0, 0, 0, 0};
+
+  // barrier in the middle of tile T's second block: tile T + 1 has landed for every wave (its
+  // loads were all issued before tile T + 2's 8) and nobody reads the stage of tile T - 1 any more
+  auto mid_for = [&](int T) {
+    return [&, T]() {
+      if (__builtin_expect(T + 1 >= nt, 0)) return;
+      __builtin_amdgcn_s_waitcnt(kWaitVm8);
+      __builtin_amdgcn_s_barrier();
+    };
   };
-  auto xcd_items = [&](int y) { return (a.nitems - y + 7) >> 3; };   // items of XCD y
-  // (positions nslot .. xcd_items(y) - 1 of XCD y are claimed; the counter words are 128 bytes
-  //  apart, and the count of finished workgroups follows them)
-  unsigned long long* const ctr = reinterpret_cast<unsigned long long*>(a.sched);
-  constexpr unsigned long long kBack = 1ull << 32;
-  __shared__ int s_next;   // the workgroup's next item, claimed during this item's start
-  int id_next = blockIdx.x;
-  // Whether w.qf already holds this item's Q: the previous item of the workgroup loaded it into
-  // the same registers as soon as its own scores were done (Q comes from HBM, and its latency
-  // was most of an item's start-up time).
-  bool q_ready = false;
-  for (int round = 0;; ++round) {
-    const int id = id_next;
-    if (id >= a.nitems || (!persist && round > 0)) break;
+  // the tile whose bytes a load for tile X fetches (see above)
+  auto load_tile = [&](int X) { return X < nt ? X : (X >= 4 ? X - 4 : X); };
+  auto nothing = []() {};
 
-    // (lane-dependent values are rebuilt for each item from an index the compiler cannot see
-    //  through, so none of them is hoisted out of the item loop and kept live across the tiles)
-    int tid = tid0;
-    asm volatile("" : "+v"(tid));
-    const int lane = tid & 63;
-    const int l32 = lane & 31;
-    const int h = lane >> 5;
-#pragma unroll
-    for (int kk = 0; kk < G::KS; ++kk)
-      w.koff[kk] = l32 * G::kRow + (((2 * kk + h) ^ kswz<D>(l32)) * 16);
-    {
-      const int g = lane >> 4, j = lane & 15;
-      const int keyl = 4 * (g >> 1) + (j >> 2);
-      const int small = 2 * (g & 1) + ((j & 3) >> 1);
-#pragma unroll
-      for (int db = 0; db < G::DB; ++db)
-        w.voff[db] = keyl * G::kRow + (((4 * db + small) ^ vswz<D>(keyl)) * 16) + 8 * (j & 1);
-    }
-
-    int rank, bh;
-    wide_item(id, a.nitems, SPLIT ? a.ntq * a.nsplit : a.ntq, a.group, a.B * a.Hkv, !SPLIT,
-              rank, bh);
-    // (with splits, the ranges of one query tile are neighbours in the order, equal in work)
-    const int split = SPLIT ? rank % a.nsplit : 0;
-    if (SPLIT) rank /= a.nsplit;
-    const int tile = CAUSAL ? (a.ntq - 1 - rank) : rank;
-    const int b = bh / a.Hq;
-    const int hq = bh - b * a.Hq;
-    const int hk = hq / a.group;
-    const int q0 = tile * kWideBM;
-    const int qw = q0 + wave * kWideRows;
-    const int off = a.Sk - a.Sq;
-
-    const uint16_t* qbase = a.q + ((size_t)(b * a.Hq + hq) * a.Sq) * D;
-    const uint16_t* kbase = a.k + ((size_t)(b * a.Hkv + hk) * a.Sk) * D;
-    const uint16_t* vbase = a.v + ((size_t)(b * a.Hkv + hk) * a.Sk) * D;
-
-    // ---- key tiles of the workgroup, and blocks of this wave ----
-    const int qend = min(q0 + kWideBM, a.Sq);         // rows of the workgroup end here
-    int kend = a.Sk;
-    if (CAUSAL) kend = min(a.Sk, max(0, qend + off));
-    const int nt_all = (kend + kBN - 1) / kBN;        // key tiles the query tile sees
-    // this workgroup's key tiles t0 .. t0 + nt - 1 (all of them without splits); below, tile and
-    // block indices count from t0, and kt0 is the first key
-    const int t0 = SPLIT ? split * nt_all / a.nsplit : 0;
-    const int nt = SPLIT ? (split + 1) * nt_all / a.nsplit - t0 : nt_all;
-    const int kt0 = t0 * kBN;
-    int nblk = 0;                                     // 32-key blocks this wave scores
-    int nunm = 0;                                     // leading blocks needing no mask
-    if (qw < a.Sq) {
-      const int qlast = min(qw + kWideRows, a.Sq) - 1;
-      int kw = a.Sk;
-      if (CAUSAL) kw = min(a.Sk, max(0, qlast + off + 1));
-      nblk = (kw + 31) / 32;
-      nunm = a.Sk / 32;
-      if (CAUSAL) nunm = min(nunm, max(0, qw + off + 1) / 32);
-      // (rows past Sq see every key of the tile: they need no mask, and are never stored)
-      nunm = min(nunm, nblk);
-      if (SPLIT) {
-        nblk = max(0, min(nblk, 2 * (t0 + nt)) - 2 * t0);
-        nunm = min(max(0, nunm - 2 * t0), nblk);
-      }
-    }
-
-#pragma unroll
-    for (int g = 0; g < 2; ++g) {
-      const int qi = qw + 32 * g + l32;
-#pragma unroll
-      for (int kk = 0; kk < G::KS; ++kk) {
-        if (q_ready)
-          ;
-        else if (qi < a.Sq)
-          w.qf[g][kk] = *reinterpret_cast<const u32x4*>(qbase + (size_t)qi * D + kk * 16 + h * 8);
-        else
-          w.qf[g][kk] = u32x4{0, 0, 0, 0};
-      }
-      w.lim[g] = CAUSAL ? min(a.Sk, qi + off + 1) : a.Sk;
-#pragma unroll
-      for (int i = 0; i < G::DB; ++i) w.o[g][i] = f32x16{};
-      w.m[g] = kNoRef;
-      w.l[g] = 0.f;
-      w.thr[g] = (kNoRef + kLazy) * a_inv_c;
-    }
-    q_ready = false;
-    TileDma<D, 4> dma;
-    dma.init(wave, lane, kbase, vbase, a.Sk);
-    // Loads: a wave's 8 loads of tile X go out one at a time between the matrix-core instructions
-    // of iterations 2X - 5 (after its barrier: loads 0..2) and 2X - 4 (loads 3..7), into the stage
-    // of tile X - 4, which no wave reads after barrier X - 3. Every load is issued, so the count of
-    // loads in flight after tile T + 1's is always 8 at barrier T: a tile past the workgroup's
-    // last loads, instead, the tile its stage already holds (X - 4, the same bytes), or for X < 4
-    // tile X itself into a stage no tile uses. Tiles 0 and 1 and the first three loads of tile 2
-    // are issued here; then wait for tile 0 (and the Q fragments, loaded earlier).
-    constexpr int kParts = 2 * G::kIPW;      // loads per wave and tile
-    static_assert(kParts == 8, "D = 128: 4 K and 4 V loads per wave and tile");
-    // the claim of the next item goes out with the tile loads and has returned by their wait
-    unsigned long long claim = 0;
-    if (dyn && wave == 0 && lane == 0) claim = atomicAdd(ctr + 16 * xs, 1ull);
-#pragma unroll
-    for (int t = 0; t < 3; ++t) {
-#pragma unroll
-      for (int j = 0; j < (t < 2 ? kParts : 3); ++j)
-        dma.issue_part_unclamped(KS[t], VS[t], kt0 + t * kBN, j);
-    }
-    __builtin_amdgcn_s_waitcnt(kWaitVm11);
-    if (dyn && wave == 0) {
-      // (the claim's two halves, as lane 0 received them; a claim fails only when every
-      //  position is taken, so failed claims move nothing that matters)
-      const unsigned f0 = __builtin_amdgcn_readfirstlane((unsigned)claim);
-      const unsigned b0 = __builtin_amdgcn_readfirstlane((unsigned)(claim >> 32));
-      int nid = (long long)f0 + b0 < xcd_items(xs) - nslot ? xs + 8 * (nslot + (int)f0) : a.nitems;
-      // (own positions all claimed: the last of another XCD's, one claim at a time; only near
-      //  the end)
-      for (int j = 1; j < 8 && nid >= a.nitems; ++j) {
-        const int y = (xs + j) & 7;
-        unsigned long long c = 0;
-        if (lane == 0) c = atomicAdd(ctr + 16 * y, kBack);
-        const unsigned fy = __builtin_amdgcn_readfirstlane((unsigned)c);
-        const unsigned by = __builtin_amdgcn_readfirstlane((unsigned)(c >> 32));
-        if ((long long)fy + by < xcd_items(y) - nslot) nid = y + 8 * (xcd_items(y) - 1 - (int)by);
-      }
-      if (lane == 0) s_next = nid;
-    }
-    if (round > 0) {
-      // Clear the dummy block's V again (every earlier load into that stage has landed now), so
-      // no other item's bytes meet its zero probabilities. The previous item's reads of the
-      // stages ended at its closing barrier.
-      u32x4* vz = reinterpret_cast<u32x4*>(VS[kStages - 1] + 32 * G::kRow);
-#pragma unroll
-      for (int i = 0; i < 32 * G::kRow / 16 / 256; ++i) vz[i * 256 + tid0] = u32x4{0, 0, 0, 0};
-    }
-    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    // (Q has landed: its fragments stay in accumulation registers for the tiles, which the
-    //  matrix cores read as B operands in place)
-#pragma unroll
-    for (int g = 0; g < 2; ++g)
-#pragma unroll
-      for (int kk = 0; kk < G::KS; ++kk) asm volatile("" : "+a"(w.qf[g][kk]));
-
-    // the dummy block before the first (slot 1, read by block 0): scores -inf, P^T zero
-    WidePipe<D> p;
-    if (nblk > 0) read_k<D>(w, KS[0], p.kf);
-    // (the constants come from an opaque register, so they are made here for each item rather
-    //  than hoisted out of the item loop and kept live across the tiles)
-    float ninf = -INFINITY;
-    asm volatile("" : "+v"(ninf));
-    const uint32_t zero = __builtin_bit_cast(uint32_t, ninf) & 0u;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) p.s1[1][r] = ninf;
-    p.mu1[1] = kNoRef;
-    p.p0[1][0] = u32x4{zero, zero, zero, zero};
-    p.p0[1][1] = u32x4{zero, zero, zero, zero};
-
-    // barrier in the middle of tile T's second block: tile T + 1 has landed for every wave (its
-    // loads were all issued before tile T + 2's 8) and nobody reads the stage of tile T - 1 any more
-    auto mid_for = [&](int T) {
-      return [&, T]() {
-        if (__builtin_expect(T + 1 >= nt, 0)) return;
-        __builtin_amdgcn_s_waitcnt(kWaitVm8);
-        __builtin_amdgcn_s_barrier();
-      };
+  // one 64-key tile (blocks 2T and 2T + 1) with its stages fixed at compile time
+  auto run_tile = [&](auto st_tag, int T) {
+    constexpr int ST = decltype(st_tag)::value;
+    char* const kc = KS[ST];                               // K/V of tile T
+    char* const vc = VS[ST];
+    char* const vp = VS[(ST + kStages - 1) % kStages];     // V of tile T - 1
+    char* const kn = KS[(ST + 1) % kStages];               // K of tile T + 1
+    char* const k2 = KS[(ST + 2) % kStages];               // tile T + 2 (loads 3..7 now)
+    char* const v2 = VS[(ST + 2) % kStages];
+    char* const k3 = KS[(ST + 3) % kStages];               // tile T + 3 (loads 0..2 now)
+    char* const v3 = VS[(ST + 3) % kStages];
+    const int k0 = kt0 + T * kBN;
+    const int kt2 = kt0 + load_tile(T + 2) * kBN, kt3 = kt0 + load_tile(T + 3) * kBN;
+    // loads 3..7 of tile T + 2 spread over block 2T (stretches 1a, 1a, 2a, 2a, 2b), loads 0..2
+    // of tile T + 3 over the stretches of block 2T + 1 after its barrier (2a, 2b, 2b)
+    auto hook0 = [&](int st, int slot) {
+      if (st == 0 && slot == 1) dma.issue_part_unclamped(k2, v2, kt2, 3);
+      if (st == 0 && slot == 5) dma.issue_part_unclamped(k2, v2, kt2, 4);
+      if (st == 2 && slot == 1) dma.issue_part_unclamped(k2, v2, kt2, 5);
+      if (st == 2 && slot == 5) dma.issue_part_unclamped(k2, v2, kt2, 6);
+      if (st == 3 && slot == 3) dma.issue_part_unclamped(k2, v2, kt2, 7);
     };
-    // the tile whose bytes a load for tile X fetches (see above)
-    auto load_tile = [&](int X) { return X < nt ? X : (X >= 4 ? X - 4 : X); };
-    auto nothing = []() {};
-
-    // one 64-key tile (blocks 2T and 2T + 1) with its stages fixed at compile time
-    auto run_tile = [&](auto st_tag, int T) {
-      constexpr int ST = decltype(st_tag)::value;
-      char* const kc = KS[ST];                               // K/V of tile T
-      char* const vc = VS[ST];
-      char* const vp = VS[(ST + kStages - 1) % kStages];     // V of tile T - 1
-      char* const kn = KS[(ST + 1) % kStages];               // K of tile T + 1
-      char* const k2 = KS[(ST + 2) % kStages];               // tile T + 2 (loads 3..7 now)
-      char* const v2 = VS[(ST + 2) % kStages];
-      char* const k3 = KS[(ST + 3) % kStages];               // tile T + 3 (loads 0..2 now)
-      char* const v3 = VS[(ST + 3) % kStages];
-      const int k0 = kt0 + T * kBN;
-      const int kt2 = kt0 + load_tile(T + 2) * kBN, kt3 = kt0 + load_tile(T + 3) * kBN;
-      // loads 3..7 of tile T + 2 spread over block 2T (stretches 1a, 1a, 2a, 2a, 2b), loads 0..2
-      // of tile T + 3 over the stretches of block 2T + 1 after its barrier (2a, 2b, 2b)
-      auto hook0 = [&](int st, int slot) {
-        if (st == 0 && slot == 1) dma.issue_part_unclamped(k2, v2, kt2, 3);
-        if (st == 0 && slot == 5) dma.issue_part_unclamped(k2, v2, kt2, 4);
-        if (st == 2 && slot == 1) dma.issue_part_unclamped(k2, v2, kt2, 5);
-        if (st == 2 && slot == 5) dma.issue_part_unclamped(k2, v2, kt2, 6);
-        if (st == 3 && slot == 3) dma.issue_part_unclamped(k2, v2, kt2, 7);
-      };
-      auto hook1 = [&](int st, int slot) {
-        if (st == 2 && slot == 3) dma.issue_part_unclamped(k3, v3, kt3, 0);
-        if (st == 3 && slot == 1) dma.issue_part_unclamped(k3, v3, kt3, 1);
-        if (st == 3 && slot == 5) dma.issue_part_unclamped(k3, v3, kt3, 2);
-      };
-      auto mid = mid_for(T);
-      const int i = 2 * T;
-      if (__builtin_expect(i < nblk, 1)) {
-        wide_iter<D, true>(w, p, vp + 32 * G::kRow, kc + 32 * G::kRow, k0, i >= nunm, h, c,
-                           a_inv_c, nothing, hook0);
-      } else {
-#pragma unroll
-        for (int j = 3; j < kParts; ++j) dma.issue_part_unclamped(k2, v2, kt2, j);
-      }
-      if (__builtin_expect(i + 1 < nblk, 1)) {
-        wide_iter<D, false>(w, p, vc, kn, k0 + 32, i + 1 >= nunm, h, c, a_inv_c, mid, hook1);
-      } else {
-        mid();
-#pragma unroll
-        for (int j = 0; j < 3; ++j) dma.issue_part_unclamped(k3, v3, kt3, j);
-      }
+    auto hook1 = [&](int st, int slot) {
+      if (st == 2 && slot == 3) dma.issue_part_unclamped(k3, v3, kt3, 0);
+      if (st == 3 && slot == 1) dma.issue_part_unclamped(k3, v3, kt3, 1);
+      if (st == 3 && slot == 5) dma.issue_part_unclamped(k3, v3, kt3, 2);
     };
+    auto mid = mid_for(T);
+    const int i = 2 * T;
+    if (__builtin_expect(i < nblk, 1)) {
+      wide_iter<D, true>(w, p, vp + 32 * G::kRow, kc + 32 * G::kRow, k0, i >= nunm, h, c,
+                         a_inv_c, nothing, hook0);
+    } else {
+#pragma unroll
+      for (int j = 3; j < kParts; ++j) dma.issue_part_unclamped(k2, v2, kt2, j);
+    }
+    if (__builtin_expect(i + 1 < nblk, 1)) {
+      wide_iter<D, false>(w, p, vc, kn, k0 + 32, i + 1 >= nunm, h, c, a_inv_c, mid, hook1);
+    } else {
+      mid();
+#pragma unroll
+      for (int j = 0; j < 3; ++j) dma.issue_part_unclamped(k3, v3, kt3, j);
+    }
+  };
 
-    for (int T = 0; T < nt; T += kStages) {
-      run_tile(std::integral_constant<int, 0>{}, T);
-      if (__builtin_expect(T + 1 >= nt, 0)) break;
-      run_tile(std::integral_constant<int, 1>{}, T + 1);
-      if (__builtin_expect(T + 2 >= nt, 0)) break;
-      run_tile(std::integral_constant<int, 2>{}, T + 2);
-      if (__builtin_expect(T + 3 >= nt, 0)) break;
-      run_tile(std::integral_constant<int, 3>{}, T + 3);
-    }
-    // The next item's Q, into the registers this item's scores are done with: the drain, the
-    // epilogue and the closing barrier run while it loads. Rows past Sq take row Sq - 1 (finite;
-    // each query row's softmax is its own, and those rows are never stored).
-    // (the next item is found here, so nothing about it is live across the tiles)
-    const int next = !persist ? a.nitems : dyn ? s_next : round_item(round + 1);
-    if (next < a.nitems) {
-      int rank_n, bh_n;
-      wide_item(next, a.nitems, a.ntq, a.group, a.B * a.Hkv, true, rank_n, bh_n);
-      const int tile_n = CAUSAL ? (a.ntq - 1 - rank_n) : rank_n;
-      const uint16_t* qbase_n = a.q + ((size_t)bh_n * a.Sq) * D;
-      const int qw_n = tile_n * kWideBM + wave * kWideRows;
-#pragma unroll
-      for (int g = 0; g < 2; ++g) {
-        const int qi = min(qw_n + 32 * g + l32, a.Sq - 1);
-#pragma unroll
-        for (int kk = 0; kk < G::KS; ++kk)
-          w.qf[g][kk] = *reinterpret_cast<const u32x4*>(qbase_n + (size_t)qi * D + kk * 16 + h * 8);
-      }
-      q_ready = true;
-    }
-    // The last block's pending work. Its V tile (tile (nblk - 1) / 2, within the last 4 tiles
-    // of the workgroup: a wave's rows end at most 192 rows before the workgroup's) is never
-    // overwritten, and every load has completed by now.
-    if (nblk > 0) {
-      const int tl = (nblk - 1) >> 1;
-      const int st = tl % kStages;
-      const char* vl = st == 0 ? VS[0] : st == 1 ? VS[1] : st == 2 ? VS[2] : VS[3];
-      // (the last block wrote slot 0 if it was even, else slot 1)
-      if ((nblk - 1) & 1) wide_drain<D, 1>(w, p, vl + 32 * G::kRow, c);
-      else wide_drain<D, 0>(w, p, vl, c);
-    }
-    // (no load may still be writing LDS when the workgroup ends; between items of one workgroup
-    //  the loads in flight are reloads of a stage's own bytes and the next Q, which the next
-    //  item's first wait covers)
-    if (!persist) __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  for (int T = 0; T < nt; T += kStages) {
+    run_tile(std::integral_constant<int, 0>{}, T);
+    if (__builtin_expect(T + 1 >= nt, 0)) break;
+    run_tile(std::integral_constant<int, 1>{}, T + 1);
+    if (__builtin_expect(T + 2 >= nt, 0)) break;
+    run_tile(std::integral_constant<int, 2>{}, T + 2);
+    if (__builtin_expect(T + 3 >= nt, 0)) break;
+    run_tile(std::integral_constant<int, 3>{}, T + 3);
+  }
+  // The last block's pending work. Its V tile (tile (nblk - 1) / 2, within the last 4 tiles
+  // of the workgroup: a wave's rows end at most 192 rows before the workgroup's) is never
+  // overwritten, and every load has completed by now.
+  if (nblk > 0) {
+    const int tl = (nblk - 1) >> 1;
+    const int st = tl % kStages;
+    const char* vl = st == 0 ? VS[0] : st == 1 ? VS[1] : st == 2 ? VS[2] : VS[3];
+    // (the last block wrote slot 0 if it was even, else slot 1)
+    if ((nblk - 1) & 1) wide_drain<D, 1>(w, p, vl + 32 * G::kRow, c);
+    else wide_drain<D, 0>(w, p, vl, c);
+  }
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);   // (no load may still be writing LDS at the end)
 
-    if (SPLIT) {
-      // ---- partial result: unnormalised O, reference max (base 2, scaled) and sum ----
-      const size_t nrows = (size_t)a.B * a.Hq * a.Sq;
-#pragma unroll
-      for (int g = 0; g < 2; ++g) {
-        const int my_q = qw + 32 * g + l32;
-        const float l_tot = xor32_sum(w.l[g]);
-        if (my_q < a.Sq) {
-          const size_t prow = (size_t)split * nrows + (size_t)(b * a.Hq + hq) * a.Sq + my_q;
-          float* po = a.part_o + prow * D;
-#pragma unroll
-          for (int db = 0; db < G::DB; ++db)
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              *reinterpret_cast<f32x4*>(po + 32 * db + 8 * e + 4 * h) =
-                  f32x4{w.o[g][db][4 * e + 0], w.o[g][db][4 * e + 1], w.o[g][db][4 * e + 2],
-                        w.o[g][db][4 * e + 3]};
-          if (h == 0)
-            *reinterpret_cast<f32x2*>(a.part_ml + prow * 2) =
-                f32x2{l_tot > 0.f ? w.m[g] : -INFINITY, l_tot};
-        }
-      }
-      return;
-    }
-
-    // ---- epilogue: normalise, store O (bf16) and LSE (natural log) ----
+  if (SPLIT) {
+    // ---- partial result: unnormalised O, reference max (base 2, scaled) and sum ----
+    const size_t nrows = (size_t)a.B * a.Hq * a.Sq;
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
       const int my_q = qw + 32 * g + l32;
       const float l_tot = xor32_sum(w.l[g]);
-      const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
-      store_o_group<G::DB>(a.o + ((size_t)(b * a.Hq + hq) * a.Sq + min(my_q, a.Sq - 1)) * D,
-                           w.o[g], inv, h, my_q < a.Sq);
       if (my_q < a.Sq) {
-        if (a.lse != nullptr && h == 0) {
-          const float lse = (l_tot > 0.f) ? (w.m[g] + log2_fast(l_tot)) * kLn2 : -INFINITY;
-          a.lse[(size_t)(b * a.Hq + hq) * a.Sq + my_q] = lse;
-        }
+        const size_t prow = (size_t)split * nrows + (size_t)(b * a.Hq + hq) * a.Sq + my_q;
+        float* po = a.part_o + prow * D;
+#pragma unroll
+        for (int db = 0; db < G::DB; ++db)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            *reinterpret_cast<f32x4*>(po + 32 * db + 8 * e + 4 * h) =
+                f32x4{w.o[g][db][4 * e + 0], w.o[g][db][4 * e + 1], w.o[g][db][4 * e + 2],
+                      w.o[g][db][4 * e + 3]};
+        if (h == 0)
+          *reinterpret_cast<f32x2*>(a.part_ml + prow * 2) =
+              f32x2{l_tot > 0.f ? w.m[g] : -INFINITY, l_tot};
       }
     }
-    id_next = next;
-    if (!persist) break;
-    // every wave's last reads of the stages (its final block) are done before the next item's
-    // loads overwrite them; the O stores stay in flight
-    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
+    return;
   }
-  if (persist) __builtin_amdgcn_s_waitcnt(kWaitVm0);
-  if (dyn && wave == 0) {
-    // Every workgroup's last claim has failed by the time it gets here; the last one to arrive
-    // clears the counters for the next launch.
-    const int ln = tid0 & 63;
-    int d = 0;
-    if (ln == 0) d = atomicAdd(a.sched + 32 * 8, 1);
-    if (__builtin_amdgcn_readfirstlane(d) == (int)gridDim.x - 1) {
-      if (ln < 8) atomicExch(ctr + 16 * ln, 0ull);
-      if (ln == 8) atomicExch(a.sched + 32 * 8, 0);
+
+  // ---- epilogue: normalise, store O (bf16) and LSE (natural log) ----
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    const int my_q = qw + 32 * g + l32;
+    const float l_tot = xor32_sum(w.l[g]);
+    const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
+    store_o_group<G::DB>(a.o + ((size_t)(b * a.Hq + hq) * a.Sq + min(my_q, a.Sq - 1)) * D,
+                         w.o[g], inv, h, my_q < a.Sq);
+    if (my_q < a.Sq) {
+      if (a.lse != nullptr && h == 0) {
+        const float lse = (l_tot > 0.f) ? (w.m[g] + log2_fast(l_tot)) * kLn2 : -INFINITY;
+        a.lse[(size_t)(b * a.Hq + hq) * a.Sq + my_q] = lse;
+      }
     }
   }
 }
@@ -871,16 +728,7 @@ hipError_t launch_fwd_bf16_wide(const FwdProblem& p, hipStream_t stream) {
     hipLaunchKernelGGL(fwd_bf16_d128_wide_split_combine, cgrid, cblock, 0, stream, a);
     return hipGetLastError();
   }
-  // One workgroup per CU walking several items when there are more items than CUs and Sk is a
-  // whole number of key tiles (the grid a multiple of 8: every workgroup stays on one XCD's
-  // items); otherwise one workgroup per item.
-  long long ngrid = nwg;
-  const int slots = (p.cus / 8) * 8;
-  if (p.Sk % kBN == 0 && slots >= 8 && nwg > slots) {
-    ngrid = slots;
-    a.sched = p.sched;
-  }
-  dim3 grid((unsigned)ngrid), block(256);
+  dim3 grid((unsigned)nwg), block(256);
   if (p.causal) hipLaunchKernelGGL(fwd_bf16_d128_causal_wide, grid, block, 0, stream, a);
   else hipLaunchKernelGGL(fwd_bf16_d128_wide, grid, block, 0, stream, a);
   return hipGetLastError();

@@ -56,7 +56,6 @@ struct FwdArgs {
   int nsplit;      // split kernel: key-range splits per query tile
   float* part_o;   // split kernel: [nsplit][B*Hq*Sq][D] unnormalised partial outputs
   float* part_ml;  // split kernel: [nsplit][B*Hq*Sq][2] (reference max, sum)
-  int* sched;      // wide kernel walking several items per workgroup: claim counters, or null
 };
 
 // Buffer resource word 3 for raw (untyped) loads on gfx9-family parts.

@@ -21,14 +21,7 @@ struct FwdProblem {
   void* workspace;   // bf16 with nsplit > 1: fwd_bf16_workspace_bytes(p, nsplit) bytes
   int mapping;       // bf16 without splits: FwdMapping, or -1 to choose by the problem
   int cus = 256;     // compute units of the device (for the choice of mapping)
-  // bf16 wide kernel: kSchedInts zeroed ints for claiming work items across XCDs (left zeroed
-  // by every launch), or null to assign the items statically
-  int* sched = nullptr;
 };
-
-// Size of the claim-counter block of the bf16 wide kernel (ints): a counter per XCD and one for
-// finished workgroups, each on its own 128-byte line.
-constexpr int kSchedInts = 9 * 32;
 
 // Work mappings of the bf16 forward without key-range splits.
 enum FwdMapping { kMapTile = 0, kMapPair = 1, kMapWide = 2 };

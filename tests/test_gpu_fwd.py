@@ -461,19 +461,18 @@ def test_fwd_wide_random_shapes(seed, dev, forced_wide):
     check_lse(lse, L, what=what + " LSE")
 
 
-# More 256-row items than compute units, with Sk a whole number of 64-key tiles: one workgroup
-# per CU walks several items in turn (B, Hq, Hkv, Sq, Sk, causal). Two or more rounds, the last
-# partial; both masks; queries ending before and after the keys (the first items of the last
-# case see no key at all); a ragged last query tile; KV heads that split evenly over the 8 XCDs
-# and ones that do not (12).
-WIDE_PERSISTENT = [
+# More 256-row items than compute units (B, Hq, Hkv, Sq, Sk, causal), compared in full: two or
+# more rounds of workgroups per CU, the last partial; both masks; queries ending before and after
+# the keys (the first items of the last case see no key at all); a ragged last query tile; KV
+# heads that split evenly over the 8 XCDs (per-XCD bundles) and ones that do not (12).
+WIDE_MANY_ITEMS = [
     (2, 48, 8, 768, 768, True), (3, 48, 8, 640, 1088, False), (1, 60, 12, 1280, 1280, True),
     (2, 72, 8, 512, 1216, True), (1, 96, 16, 900, 640, True),
 ]
 
 
-@pytest.mark.parametrize("shape", WIDE_PERSISTENT, ids=lambda s: "x".join(map(str, s)))
-def test_fwd_wide_persistent(shape, dev, forced_wide):
+@pytest.mark.parametrize("shape", WIDE_MANY_ITEMS, ids=lambda s: "x".join(map(str, s)))
+def test_fwd_wide_many_items(shape, dev, forced_wide):
     B, Hq, Hkv, Sq, Sk, causal = shape
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     assert ((Sq + 255) // 256) * B * Hq > cus and Sk % 64 == 0
@@ -485,10 +484,9 @@ def test_fwd_wide_persistent(shape, dev, forced_wide):
     check_lse(lse, L, what=f"{shape} LSE")
 
 
-def test_fwd_wide_persistent_is_deterministic(dev, forced_wide):
-    """Workgroups that walk several items give identical bits on repeated launches, and the
-    same bits as a problem of one item per workgroup would for the same rows (the batch entry
-    alone, 144 items)."""
+def test_fwd_wide_many_items_is_deterministic(dev, forced_wide):
+    """A many-item problem gives identical bits on repeated launches, and each batch entry the
+    bits of that entry alone (144 items, a different placement of its items on the XCDs)."""
     q, k, v = W.fwd_inputs(2, 48, 8, 768, 768, 128, seed=21)
     qg, kg, vg = (_gpu(x, dev, torch.bfloat16) for x in (q, k, v))
     ref, ref_l = A.attn_fwd(qg, kg, vg, causal=True)
@@ -501,10 +499,9 @@ def test_fwd_wide_persistent_is_deterministic(dev, forced_wide):
     assert torch.equal(o1[0], ref[1]) and torch.equal(l1[0], ref_l[1])
 
 
-def test_fwd_wide_persistent_two_streams(dev, forced_wide):
+def test_fwd_wide_many_items_two_streams(dev, forced_wide):
     """The same many-item problem launched alternately on two streams without synchronising
-    between them: each stream claims items through its own counters, and every launch gives the
-    bits of a launch alone."""
+    between them: every launch gives the bits of a launch alone."""
     q, k, v = W.fwd_inputs(1, 60, 12, 1280, 1280, 128, seed=22)
     qg, kg, vg = (_gpu(x, dev, torch.bfloat16) for x in (q, k, v))
     ref, ref_l = A.attn_fwd(qg, kg, vg, causal=True)

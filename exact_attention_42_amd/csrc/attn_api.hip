@@ -182,6 +182,53 @@ int get_workspace_locked(void* stream, size_t need, void** out) {
   return ATTN_OK;
 }
 
+// Claim block of the wide forward for (current device, stream), at least `words` words: its
+// item marks start below any launch mark, and each launch takes a larger mark, so nothing is
+// cleared between launches. Launches on one stream run one after another and never share a
+// block. None on a stream being captured (a replayed graph would repeat its launch mark) or on
+// the per-thread default stream (one handle for many streams): the kernel then runs each item
+// on its own workgroup only. The caller holds g_ws_mutex until its kernels are enqueued.
+struct ClaimBlock {
+  unsigned long long* ptr = nullptr;
+  size_t words = 0;
+  unsigned long long epoch = 0;
+};
+std::map<std::pair<int, void*>, ClaimBlock> g_claim;
+
+void claim_block_locked(void* stream, size_t words, unsigned long long** out,
+                        unsigned long long* epoch) {
+  *out = nullptr;
+  if (static_cast<hipStream_t>(stream) == hipStreamPerThread) return;
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  int dev = 0;
+  if (hipStreamIsCapturing(static_cast<hipStream_t>(stream), &cap) != hipSuccess ||
+      cap != hipStreamCaptureStatusNone || hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return;
+  }
+  ClaimBlock& c = g_claim[{dev, stream}];
+  if (c.words < words) {
+    const size_t n = std::max(words, std::max(c.words * 2, (size_t)4096));
+    void* p = nullptr;
+    if (hipMalloc(&p, n * sizeof(unsigned long long)) != hipSuccess) {
+      (void)hipGetLastError();
+      return;
+    }
+    if (hipMemsetAsync(p, 0, n * sizeof(unsigned long long),
+                       static_cast<hipStream_t>(stream)) != hipSuccess) {
+      (void)hipGetLastError();
+      (void)hipFree(p);
+      return;
+    }
+    if (c.ptr) g_retired.push_back({dev, c.ptr});
+    c.ptr = static_cast<unsigned long long*>(p);
+    c.words = n;
+  }
+  c.epoch += 2;   // even marks for owners; stealers mark with the odd value above
+  *out = c.ptr;
+  *epoch = c.epoch;
+}
+
 // Device address of `scratch` on the current device, looked up once per device (with that
 // device current) and kept; a fixed table, so the lookup allocates nothing either.
 constexpr int kMaxDevices = 64;
@@ -238,6 +285,14 @@ int run_fwd(bool f32, const void* q, const void* k, const void* v, void* o, floa
         ws_lock.lock();
         if (int rc = get_workspace_locked(stream, need, &p.workspace)) return rc;
       }
+    }
+  }
+  if (!f32) {
+    // more wide-kernel items than CUs: workgroups that finish early take items of slower XCDs
+    const long long items = attn::fwd_wide_items(p);
+    if (items > p.cus) {
+      if (!ws_lock.owns_lock()) ws_lock.lock();
+      claim_block_locked(stream, attn::wide_claim_words(items), &p.claim, &p.epoch);
     }
   }
   hipError_t e = f32 ? attn::launch_fwd_f32(p, static_cast<hipStream_t>(stream))
@@ -585,10 +640,16 @@ void attn_release_workspace(void) {
       if (hipSetDevice(kv.first.first) == hipSuccess) (void)hipFree(kv.second.ptr);
     }
   }
+  for (auto& kv : g_claim) {
+    if (kv.second.ptr) {
+      if (hipSetDevice(kv.first.first) == hipSuccess) (void)hipFree(kv.second.ptr);
+    }
+  }
   for (auto& r : g_retired) {
     if (hipSetDevice(r.first) == hipSuccess) (void)hipFree(r.second);
   }
   g_ws.clear();
+  g_claim.clear();
   g_retired.clear();
   if (have_cur) (void)hipSetDevice(cur);
 }

@@ -641,6 +641,13 @@ int fwd_bf16_mapping(const FwdProblem& p, int cus) {
   return (p.causal && ntq <= kPairMaxTiles) ? kMapPair : kMapTile;
 }
 
+long long fwd_wide_items(const FwdProblem& p) {
+  if (p.nsplit > 1 || p.D != 128) return 0;
+  const int mapping = p.mapping >= 0 ? p.mapping : fwd_bf16_mapping(p, p.cus);
+  if (mapping != kMapWide) return 0;
+  return (long long)((p.Sq + kWideRows - 1) / kWideRows) * p.B * p.Hq;
+}
+
 size_t fwd_bf16_workspace_bytes(const FwdProblem& p, int nsplit) {
   if (nsplit <= 1) return 0;
   const size_t rows = (size_t)nsplit * p.B * p.Hq * p.Sq;

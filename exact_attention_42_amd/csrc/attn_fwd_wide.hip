@@ -53,6 +53,11 @@ constexpr int kWideBM = 4 * kWideRows;         // query rows per workgroup
 // workgroup's last, so its stage is never reloaded and the wave can finish its last block
 // after the loop.
 constexpr int kStages = 4;
+// Workgroups per XCD that take other XCDs' last items (a fast XCD's share of the spread between
+// XCDs, in light items of a few to a few tens of microseconds each).
+constexpr int kTakers = 128;
+// Words of the claim block before the item marks (the counters and the "nothing left" mark).
+constexpr int kClaimHead = 9 * 16;
 
 // s_waitcnt immediates, gfx9 encoding (vmcnt in bits 3:0 and 15:14, expcnt and lgkmcnt free)
 constexpr int kWaitVm0 = 0x0F70;
@@ -409,11 +414,13 @@ __device__ __forceinline__ void wide_item(int id, int nitems, int ntq, int group
   bh = kvh * group + (r - rank * group);
 }
 
-// SPLIT: the workgroup covers one of a.nsplit contiguous ranges of its query tile's key tiles
-// and writes its unnormalised partial result (O, reference max, sum) to the workspace; a merge
-// kernel combines the ranges (for problems with too few query tiles to fill the device).
+// One work item on the workgroup. SPLIT: the workgroup covers one of a.nsplit contiguous ranges
+// of its query tile's key tiles and writes its unnormalised partial result (O, reference max,
+// sum) to the workspace; a merge kernel combines the ranges (for problems with too few query
+// tiles to fill the device). `claimed`: the item is this workgroup's own, marked in the claim
+// block as the work starts; if a workgroup of another XCD took it first, this one stops there.
 template <int D, bool CAUSAL, bool SPLIT>
-__device__ __forceinline__ void fwd_wide_body(const FwdArgs& a) {
+__device__ __forceinline__ void wide_item_body(const FwdArgs& a, int id, bool claimed) {
   using G = Geo<D, 4>;
   // (The V stages are placed in the low 64 KiB, where a stage's base fits the 16-bit offset
   //  field of the transposing reads; the LDS layout orders these objects by name.)
@@ -435,7 +442,7 @@ __device__ __forceinline__ void fwd_wide_body(const FwdArgs& a) {
   const int h = lane >> 5;
 
   int rank, bh;
-  wide_item(blockIdx.x, a.nitems, SPLIT ? a.ntq * a.nsplit : a.ntq, a.group, a.B * a.Hkv, rank,
+  wide_item(id, a.nitems, SPLIT ? a.ntq * a.nsplit : a.ntq, a.group, a.B * a.Hkv, rank,
             bh);
   // (with splits, the ranges of one query tile are neighbours in the order, equal in work)
   const int split = SPLIT ? rank % a.nsplit : 0;
@@ -540,6 +547,10 @@ __device__ __forceinline__ void fwd_wide_body(const FwdArgs& a) {
   // are issued here; then wait for tile 0 (and the Q fragments, loaded earlier).
   constexpr int kParts = 2 * G::kIPW;      // loads per wave and tile
   static_assert(kParts == 8, "D = 128: 4 K and 4 V loads per wave and tile");
+  // (the item's claim mark goes out with the loads, and has returned by their wait)
+  __shared__ int s_stolen;
+  unsigned long long took = 0;
+  if (claimed && wave == 0 && lane == 0) took = atomicMax(a.claim + kClaimHead + id, a.epoch);
 #pragma unroll
   for (int t = 0; t < 3; ++t) {
 #pragma unroll
@@ -547,9 +558,15 @@ __device__ __forceinline__ void fwd_wide_body(const FwdArgs& a) {
       dma.issue_part_unclamped(KS[t], VS[t], kt0 + t * kBN, j);
   }
   __builtin_amdgcn_s_waitcnt(kWaitVm11);
+  if (claimed && wave == 0 && lane == 0) s_stolen = took == (a.epoch | 1ull);
   __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
+  if (claimed && s_stolen) {
+    // another XCD's workgroup runs this item: no load may still be writing LDS at the end
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    return;
+  }
 
   // the dummy block before the first (slot 1, read by block 0): scores -inf, P^T zero
   WidePipe<D> p;
@@ -682,6 +699,68 @@ __device__ __forceinline__ void fwd_wide_body(const FwdArgs& a) {
   }
 }
 
+// Claims the last unclaimed item of another XCD (one lane; a.nitems when nothing is left). The
+// claim block holds per XCD x a word at 16 * x counting this launch's claims from the back of
+// x's order, at 16 * 8 the launch's "nothing left" mark, and from kClaimHead on a mark per item.
+// Launch marks grow from launch to launch, so an item mark below a.epoch is unclaimed; owners
+// raise it to a.epoch and takers to a.epoch + 1, with an atomic maximum, so a mark never lowers
+// another (a taker that finds the owner there leaves the owner's claim as it is). A counter word
+// carries the launch (a.epoch / 2) in its upper half; the first claim of a launch finds an
+// earlier launch's there and restarts it.
+__device__ __forceinline__ int wide_take(const FwdArgs& a, int xs) {
+  unsigned long long* const ctr = a.claim;
+  if (__hip_atomic_load(ctr + 16 * 8, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.epoch)
+    return a.nitems;
+  const unsigned long long launch = a.epoch >> 1;
+  for (int j = 1; j < 8; ++j) {
+    const int x = (xs + j) & 7;
+    const int cnt = (a.nitems - x + 7) >> 3;   // items of XCD x
+    unsigned long long w = atomicAdd(ctr + 16 * x, 1ull);
+    long long b;
+    if ((w >> 32) == (launch & 0xffffffffull)) {
+      b = (long long)(w & 0xffffffffull);
+    } else {
+      const unsigned long long fresh = ((launch & 0xffffffffull) << 32) | 1ull;
+      if (atomicCAS(ctr + 16 * x, w + 1, fresh) == w + 1) {
+        b = 0;
+      } else {
+        w = atomicAdd(ctr + 16 * x, 1ull);
+        if ((w >> 32) != (launch & 0xffffffffull)) continue;   // (left to others)
+        b = (long long)(w & 0xffffffffull);
+      }
+    }
+    if (b >= cnt) continue;
+    const int id = x + 8 * (cnt - 1 - (int)b);
+    if (atomicMax(a.claim + kClaimHead + id, a.epoch | 1ull) < a.epoch) return id;
+    // its owner has it: XCD x's owners have reached the back of its order
+  }
+  atomicExch(ctr + 16 * 8, a.epoch);
+  return a.nitems;
+}
+
+// The wide kernel's workgroups, one item each. Items are workgroups 0 .. nitems - 1; with a
+// claim block, the workgroups past them each take the last unclaimed item of another XCD, or
+// end at once when none is left. They are dispatched after all of their own XCD's items, so
+// they start as that XCD finishes its share: under this load the XCDs run at clocks up to
+// several percent apart, and the faster ones then take over the slower ones' last (lightest)
+// items. (Each takes one item: a loop over items here would be a second copy of the item code,
+// and with two copies the compiler lays out the tile loop less well.)
+template <int D, bool CAUSAL, bool SPLIT>
+__device__ __forceinline__ void fwd_wide_body(const FwdArgs& a) {
+  int id = blockIdx.x;
+  const bool taker = !SPLIT && a.claim != nullptr && id >= a.nitems;
+  if (taker) {
+    __shared__ int s_take;
+    if (threadIdx.x == 0) s_take = wide_take(a, blockIdx.x & 7);
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    id = s_take;
+    if (id >= a.nitems) return;
+  }
+  wide_item_body<D, CAUSAL, SPLIT>(a, id, !SPLIT && a.claim != nullptr && !taker);
+}
+
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void fwd_bf16_d128_causal_wide(FwdArgs a) { fwd_wide_body<128, true, false>(a); }
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -728,7 +807,13 @@ hipError_t launch_fwd_bf16_wide(const FwdProblem& p, hipStream_t stream) {
     hipLaunchKernelGGL(fwd_bf16_d128_wide_split_combine, cgrid, cblock, 0, stream, a);
     return hipGetLastError();
   }
-  dim3 grid((unsigned)nwg), block(256);
+  // with a claim block, kTakers workgroups per XCD after the items take over other XCDs' last
+  // items (those that find none end at once)
+  a.claim = p.claim;
+  a.epoch = p.epoch;
+  const long long ngrid = nwg + (a.claim != nullptr ? 8 * kTakers : 0);
+  if (ngrid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  dim3 grid((unsigned)ngrid), block(256);
   if (p.causal) hipLaunchKernelGGL(fwd_bf16_d128_causal_wide, grid, block, 0, stream, a);
   else hipLaunchKernelGGL(fwd_bf16_d128_wide, grid, block, 0, stream, a);
   return hipGetLastError();

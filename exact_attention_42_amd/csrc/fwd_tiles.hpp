@@ -56,6 +56,10 @@ struct FwdArgs {
   int nsplit;      // split kernel: key-range splits per query tile
   float* part_o;   // split kernel: [nsplit][B*Hq*Sq][D] unnormalised partial outputs
   float* part_ml;  // split kernel: [nsplit][B*Hq*Sq][2] (reference max, sum)
+  // wide kernel: per-XCD claim counters, the launch's "nothing left" word and the work items'
+  // claim marks (null: no workgroup takes another's item), and this launch's mark
+  unsigned long long* claim;
+  unsigned long long epoch;
 };
 
 // Buffer resource word 3 for raw (untyped) loads on gfx9-family parts.

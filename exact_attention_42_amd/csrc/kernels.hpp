@@ -21,7 +21,20 @@ struct FwdProblem {
   void* workspace;   // bf16 with nsplit > 1: fwd_bf16_workspace_bytes(p, nsplit) bytes
   int mapping;       // bf16 without splits: FwdMapping, or -1 to choose by the problem
   int cus = 256;     // compute units of the device (for the choice of mapping)
+  // bf16 wide kernel without splits: wide_claim_words(items) words that no other launch uses
+  // at the same time, and a launch mark (even, larger than any earlier launch's on them); null
+  // runs each item on its own workgroup only
+  unsigned long long* claim = nullptr;
+  unsigned long long epoch = 0;
 };
+
+// Words of the wide kernel's claim block for `items` work items: the per-XCD counters and the
+// "nothing left" word, each on its own 128-byte line, then a mark per item.
+inline size_t wide_claim_words(long long items) { return 9 * 16 + (size_t)items; }
+
+// Work items of the bf16 wide kernel for a problem (0 when the problem does not run on it
+// without key-range splits).
+long long fwd_wide_items(const FwdProblem& p);
 
 // Work mappings of the bf16 forward without key-range splits.
 enum FwdMapping { kMapTile = 0, kMapPair = 1, kMapWide = 2 };

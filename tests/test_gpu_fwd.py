@@ -499,6 +499,27 @@ def test_fwd_wide_many_items_is_deterministic(dev, forced_wide):
     assert torch.equal(o1[0], ref[1]) and torch.equal(l1[0], ref_l[1])
 
 
+def test_fwd_wide_many_items_sizes_in_turn(dev, forced_wide):
+    """Many-item problems of different sizes launched one after another on one stream with no
+    synchronisation between them (fewer items, then more, then fewer again): each output
+    matches the oracle's."""
+    shapes = [(2, 72, 8, 512, 1216, True), (1, 96, 16, 900, 640, True),
+              (2, 48, 8, 768, 768, True), (3, 48, 8, 640, 1088, False),
+              (1, 60, 12, 1280, 1280, True)]
+    scale = np.float32(1 / np.sqrt(128))
+    runs = []
+    for i, (B, Hq, Hkv, Sq, Sk, causal) in enumerate(shapes):
+        q, k, v = W.fwd_inputs(B, Hq, Hkv, Sq, Sk, 128, seed=7900 + i)
+        o, lse = A.attn_fwd(_gpu(q, dev, torch.bfloat16), _gpu(k, dev, torch.bfloat16),
+                            _gpu(v, dev, torch.bfloat16), causal=causal, scale=float(scale))
+        runs.append((q, k, v, causal, o, lse))
+    torch.cuda.synchronize()
+    for (q, k, v, causal, o, lse), shape in zip(runs, shapes):
+        O, L = oracle.attention(q, k, v, causal=causal, scale=scale)
+        check_bf16(to_np(o), O, what=f"{shape} O")
+        check_lse(to_np(lse), L, what=f"{shape} LSE")
+
+
 def test_fwd_wide_many_items_two_streams(dev, forced_wide):
     """The same many-item problem launched alternately on two streams without synchronising
     between them: every launch gives the bits of a launch alone."""

@@ -40,6 +40,15 @@
  * A replaced buffer is not freed until attn_release_workspace (kernels enqueued earlier may
  * still read it). The library workspace is never used on a stream that is being captured into
  * a graph: such a call returns ATTN_ERR_WORKSPACE; pass a caller workspace instead.
+ *
+ * Claim block. A bf16 forward with D = 128 and more 256-row work items than the device has
+ * compute units lets workgroups that finish early take the last items of slower XCDs. The
+ * items' claim marks live in a small block the library owns per (device, stream), at least
+ * 8 * (144 + items) bytes, allocated and cleared on first use, replaced (like the workspace)
+ * when a call needs more, never cleared again (every launch takes larger marks) and freed by
+ * attn_release_workspace. On a stream being captured, or on the per-thread default stream, or
+ * if the block cannot be allocated, the call runs without it: each item on its own workgroup,
+ * with the same results bit for bit.
  */
 #ifndef EXACT_ATTENTION_ATTN_H
 #define EXACT_ATTENTION_ATTN_H
@@ -295,8 +304,9 @@ const char* attn_status_string(int status);
 /* Detail of the last failed call on this thread ("" if none). */
 const char* attn_last_error(void);
 
-/* Frees every library-owned workspace, including replaced ones (synchronises the devices
- * that hold them). No call may be running or enqueued-and-unfinished when it is called. */
+/* Frees every library-owned workspace and claim block, including replaced ones (synchronises
+ * the devices that hold them). No call may be running or enqueued-and-unfinished when it is
+ * called. */
 void attn_release_workspace(void);
 
 /* ABI version of this header: 10. */

@@ -62,8 +62,9 @@ constexpr int kPairMaxTiles = 64;
 constexpr int kMaxFwdSplits = 8;
 
 // SPLIT: the workgroup covers one of a.nsplit contiguous ranges of the query tile's key tiles
-// and writes its unnormalised partial result (O, reference max, sum) to the workspace; the
-// split combine kernel merges the ranges. Otherwise it covers all the tile's keys.
+// and writes that range's own output (bf16, normalised by the range's sum), reference max and
+// sum to the workspace; the split combine kernel merges the ranges. Otherwise it covers all
+// the tile's keys.
 template <int D, bool CAUSAL, bool SPLIT>
 __device__ __forceinline__ void fwd_tile_body(const FwdArgs& a) {
   using G = Geo<D, 4>;
@@ -163,24 +164,15 @@ __device__ __forceinline__ void fwd_tile_body(const FwdArgs& a) {
   }
 
   if (SPLIT) {
-    // ---- partial result: unnormalised O, reference max (base 2, scaled) and sum ----
+    // ---- partial result: this key range's own output (bf16), reference max (base 2,
+    //      scaled) and sum ----
     const float l_tot = xor32_sum(w.l_run);
-    if (my_q < a.Sq) {
-      const size_t prow = (size_t)split * BH * a.Sq + (size_t)bh * a.Sq + my_q;
-      float* po = a.part_o + prow * D;
-#pragma unroll
-      for (int db = 0; db < G::DB; ++db)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int d = 32 * db + 8 * g + 4 * h;
-          *reinterpret_cast<f32x4*>(po + d) =
-              f32x4{w.o[db][4 * g + 0], w.o[db][4 * g + 1], w.o[db][4 * g + 2],
-                    w.o[db][4 * g + 3]};
-        }
-      if (h == 0)
-        *reinterpret_cast<f32x2*>(a.part_ml + prow * 2) =
-            f32x2{l_tot > 0.f ? w.mref : -INFINITY, l_tot};
-    }
+    const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
+    const size_t prow = (size_t)split * BH * a.Sq + (size_t)bh * a.Sq + min(my_q, a.Sq - 1);
+    store_o_group<G::DB>(a.part_o + prow * D, w.o, inv, h, my_q < a.Sq);
+    if (my_q < a.Sq && h == 0)
+      *reinterpret_cast<f32x2*>(a.part_ml + prow * 2) =
+          f32x2{l_tot > 0.f ? w.mref : -INFINITY, l_tot};
     return;
   }
 
@@ -651,7 +643,7 @@ long long fwd_wide_items(const FwdProblem& p) {
 size_t fwd_bf16_workspace_bytes(const FwdProblem& p, int nsplit) {
   if (nsplit <= 1) return 0;
   const size_t rows = (size_t)nsplit * p.B * p.Hq * p.Sq;
-  return rows * p.D * sizeof(float) + rows * 2 * sizeof(float);
+  return rows * p.D * sizeof(uint16_t) + rows * 2 * sizeof(float);
 }
 
 hipError_t launch_fwd_bf16(const FwdProblem& p, hipStream_t stream) {
@@ -679,8 +671,8 @@ hipError_t launch_fwd_bf16(const FwdProblem& p, hipStream_t stream) {
   if (a.nsplit > 1 && p.D == 128 && p.Sq >= kWideRows) return launch_fwd_bf16_wide(p, stream);
   if (a.nsplit > 1) {
     const size_t rows = (size_t)a.nsplit * p.B * p.Hq * p.Sq;
-    a.part_o = static_cast<float*>(p.workspace);
-    a.part_ml = a.part_o + rows * p.D;
+    a.part_o = static_cast<uint16_t*>(p.workspace);
+    a.part_ml = reinterpret_cast<float*>(a.part_o + rows * p.D);
     const long long nwg = (long long)a.ntq * a.nsplit * p.B * p.Hq;
     if (nwg == 0) return hipSuccess;
     if (nwg > 0x7fffffffLL) return hipErrorInvalidConfiguration;

@@ -48,7 +48,7 @@ struct PagedArgs {
   int num_blocks;           // pool size; <= 0: entries are not range-checked
   float c;                  // scale * log2(e), > 0
   int nsplit;
-  float* part_o;            // [nsplit][T * Hq][D]
+  uint16_t* part_o;         // [nsplit][T * Hq][D] bf16 output of each key range alone
   float* part_ml;           // [nsplit][T * Hq][2]
 };
 
@@ -266,23 +266,13 @@ __device__ __forceinline__ void fwd_paged_body(const PagedArgs& a) {
     const float l_tot = xor32_sum(w.l_run);
     const size_t row = (size_t)(qs + min(my_q, Sq - 1)) * a.Hq + hq;   // (Sq >= 1 here)
     if (SPLIT) {
-      if (my_q < Sq) {
-        // unnormalised O, reference max (base 2, scaled) and sum of this key range
-        const size_t prow = (size_t)split * R + row;
-        float* po = a.part_o + prow * D;
-#pragma unroll
-        for (int db = 0; db < G::DB; ++db)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int d = 32 * db + 8 * g + 4 * h;
-            *reinterpret_cast<f32x4*>(po + d) =
-                f32x4{w.o[db][4 * g + 0], w.o[db][4 * g + 1], w.o[db][4 * g + 2],
-                      w.o[db][4 * g + 3]};
-          }
-        if (h == 0)
-          *reinterpret_cast<f32x2*>(a.part_ml + prow * 2) =
-              f32x2{l_tot > 0.f ? w.mref : -INFINITY, l_tot};
-      }
+      // this key range's own output (bf16), reference max (base 2, scaled) and sum
+      const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
+      const size_t prow = (size_t)split * R + row;
+      store_o_group<G::DB>(a.part_o + prow * D, w.o, inv, h, my_q < Sq);
+      if (my_q < Sq && h == 0)
+        *reinterpret_cast<f32x2*>(a.part_ml + prow * 2) =
+            f32x2{l_tot > 0.f ? w.mref : -INFINITY, l_tot};
     } else {
       const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
       store_o_group<G::DB>(a.o + row * D, w.o, inv, h, my_q < Sq);
@@ -348,7 +338,7 @@ int fwd_paged_splits(const PagedProblem& p, int cus) {
 size_t fwd_paged_workspace_bytes(const PagedProblem& p, int nsplit) {
   if (nsplit <= 1) return 0;
   const size_t rows = (size_t)nsplit * p.T * p.Hq;
-  return rows * p.D * sizeof(float) + rows * 2 * sizeof(float);
+  return rows * p.D * sizeof(uint16_t) + rows * 2 * sizeof(float);
 }
 
 hipError_t launch_fwd_paged(const PagedProblem& p, hipStream_t stream) {
@@ -378,8 +368,8 @@ hipError_t launch_fwd_paged(const PagedProblem& p, hipStream_t stream) {
   dim3 grid((unsigned)nwg), block(256);
   if (a.nsplit > 1) {
     const size_t rows = (size_t)a.nsplit * p.T * p.Hq;
-    a.part_o = static_cast<float*>(p.workspace);
-    a.part_ml = a.part_o + rows * p.D;
+    a.part_o = static_cast<uint16_t*>(p.workspace);
+    a.part_ml = reinterpret_cast<float*>(a.part_o + rows * p.D);
     const size_t nrows = (size_t)p.T * p.Hq;
     const int rows_per_block = 256 / (p.D / 4);
     dim3 cgrid((unsigned)((nrows + rows_per_block - 1) / rows_per_block)), cblock(256);

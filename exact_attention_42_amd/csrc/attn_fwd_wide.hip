@@ -415,9 +415,9 @@ __device__ __forceinline__ void wide_item(int id, int nitems, int ntq, int group
 }
 
 // One work item on the workgroup. SPLIT: the workgroup covers one of a.nsplit contiguous ranges
-// of its query tile's key tiles and writes its unnormalised partial result (O, reference max,
-// sum) to the workspace; a merge kernel combines the ranges (for problems with too few query
-// tiles to fill the device). `claimed`: the item is this workgroup's own, marked in the claim
+// of its query tile's key tiles and writes that range's own output (bf16, normalised by the
+// range's sum), reference max and sum to the workspace; a merge kernel combines the ranges
+// (for problems with too few query tiles to fill the device). `claimed`: the item is this workgroup's own, marked in the claim
 // block as the work starts; if a workgroup of another XCD took it first, this one stops there.
 template <int D, bool CAUSAL, bool SPLIT>
 __device__ __forceinline__ void wide_item_body(const FwdArgs& a, int id, bool claimed) {
@@ -658,26 +658,20 @@ __device__ __forceinline__ void wide_item_body(const FwdArgs& a, int id, bool cl
   __builtin_amdgcn_s_waitcnt(kWaitVm0);   // (no load may still be writing LDS at the end)
 
   if (SPLIT) {
-    // ---- partial result: unnormalised O, reference max (base 2, scaled) and sum ----
+    // ---- partial result: this key range's own output (bf16), reference max (base 2,
+    //      scaled) and sum ----
     const size_t nrows = (size_t)a.B * a.Hq * a.Sq;
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
       const int my_q = qw + 32 * g + l32;
       const float l_tot = xor32_sum(w.l[g]);
-      if (my_q < a.Sq) {
-        const size_t prow = (size_t)split * nrows + (size_t)(b * a.Hq + hq) * a.Sq + my_q;
-        float* po = a.part_o + prow * D;
-#pragma unroll
-        for (int db = 0; db < G::DB; ++db)
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            *reinterpret_cast<f32x4*>(po + 32 * db + 8 * e + 4 * h) =
-                f32x4{w.o[g][db][4 * e + 0], w.o[g][db][4 * e + 1], w.o[g][db][4 * e + 2],
-                      w.o[g][db][4 * e + 3]};
-        if (h == 0)
-          *reinterpret_cast<f32x2*>(a.part_ml + prow * 2) =
-              f32x2{l_tot > 0.f ? w.m[g] : -INFINITY, l_tot};
-      }
+      const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
+      const size_t prow =
+          (size_t)split * nrows + (size_t)(b * a.Hq + hq) * a.Sq + min(my_q, a.Sq - 1);
+      store_o_group<G::DB>(a.part_o + prow * D, w.o[g], inv, h, my_q < a.Sq);
+      if (my_q < a.Sq && h == 0)
+        *reinterpret_cast<f32x2*>(a.part_ml + prow * 2) =
+            f32x2{l_tot > 0.f ? w.m[g] : -INFINITY, l_tot};
     }
     return;
   }
@@ -797,8 +791,8 @@ hipError_t launch_fwd_bf16_wide(const FwdProblem& p, hipStream_t stream) {
     // the key ranges of each query tile, then their merge (workspace as for the other forward
     // kernels' splits: fwd_bf16_workspace_bytes)
     const size_t nrows = (size_t)p.B * p.Hq * p.Sq;
-    a.part_o = static_cast<float*>(p.workspace);
-    a.part_ml = a.part_o + (size_t)a.nsplit * nrows * p.D;
+    a.part_o = static_cast<uint16_t*>(p.workspace);
+    a.part_ml = reinterpret_cast<float*>(a.part_o + (size_t)a.nsplit * nrows * p.D);
     dim3 grid((unsigned)nwg), block(256);
     if (p.causal) hipLaunchKernelGGL(fwd_bf16_d128_causal_wide_split, grid, block, 0, stream, a);
     else hipLaunchKernelGGL(fwd_bf16_d128_wide_split, grid, block, 0, stream, a);

@@ -54,8 +54,8 @@ struct FwdArgs {
   int nitems;      // pair kernel: B * Hq * npairs
   float c;         // scale * log2(e), > 0
   int nsplit;      // split kernel: key-range splits per query tile
-  float* part_o;   // split kernel: [nsplit][B*Hq*Sq][D] unnormalised partial outputs
-  float* part_ml;  // split kernel: [nsplit][B*Hq*Sq][2] (reference max, sum)
+  uint16_t* part_o;  // split kernels: [nsplit][B*Hq*Sq][D] bf16 output of each key range alone
+  float* part_ml;     // split kernels: [nsplit][B*Hq*Sq][2] (reference max, sum) of each range
   // wide kernel: per-XCD claim counters, the launch's "nothing left" word and the work items'
   // claim marks (null: no workgroup takes another's item), and this launch's mark
   unsigned long long* claim;
@@ -375,9 +375,15 @@ __device__ __forceinline__ void fwd_split_combine_body(const FwdArgs& a, size_t 
       const size_t pr = (size_t)s * nrows + row;
       const f32x2 ml = *reinterpret_cast<const f32x2*>(a.part_ml + pr * 2);
       if (ml[0] == -INFINITY) continue;
-      const float wgt = exp2_fast(ml[0] - M);
-      L += wgt * ml[1];
-      O += wgt * *reinterpret_cast<const f32x4*>(a.part_o + pr * D + c4);
+      // (each range's output is its own softmax-weighted sum: weight it by its share of the
+      //  whole row's sum)
+      const float wl = exp2_fast(ml[0] - M) * ml[1];
+      L += wl;
+      const u32x2 ov = *reinterpret_cast<const u32x2*>(a.part_o + pr * D + c4);
+      O += wl * f32x4{__builtin_bit_cast(float, ov[0] << 16),
+                      __builtin_bit_cast(float, ov[0] & 0xffff0000u),
+                      __builtin_bit_cast(float, ov[1] << 16),
+                      __builtin_bit_cast(float, ov[1] & 0xffff0000u)};
     }
   }
   const float inv = (L > 0.f) ? 1.f / L : 0.f;

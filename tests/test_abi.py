@@ -115,11 +115,11 @@ def test_fwd_paged_empty_problem_is_a_no_op(kw):
 
 def test_fwd_paged_workspace_size():
     # 128 query tiles on 256 CUs: ceil(2 * 256 / 128) = 4 key ranges per tile, each of the
-    # T * Hq rows with D + 2 floats per range
+    # T * Hq rows with D bf16 outputs and 2 floats (max, sum) per range
     if A.attn_fwd_paged_workspace_bytes(1, 512, 32, 8, 128, 512, 4096, 1) == 0:
         pytest.skip("device reports other than 256 CUs")
     assert A.attn_fwd_paged_workspace_bytes(1, 512, 32, 8, 128, 512, 4096, 1) == \
-        4 * 512 * 32 * 130 * 4
+        4 * 512 * 32 * (128 * 2 + 2 * 4)
     # enough query tiles: no splits
     assert A.attn_fwd_paged_workspace_bytes(8, 32768, 32, 8, 128, 4096, 4096, 1) == 0
     for bad in [(-1, 1, 1, 1, 64, 1, 1, 1), (1, 1, 6, 4, 64, 1, 1, 1), (1, 1, 1, 1, 80, 1, 1, 1),

@@ -63,6 +63,33 @@ constexpr int kClaimHead = 9 * 16;
 constexpr int kWaitVm0 = 0x0F70;
 constexpr int kWaitVm8 = 0x0F78;
 constexpr int kWaitVm11 = 0x0F7B;
+constexpr int kWaitVm16 = 0x4F70;   // (vmcnt's two high bits sit at 15:14)
+
+typedef __attribute__((address_space(3))) char lds_char;
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const lds_char*)p;
+}
+
+// Raw buffer descriptor (base, no stride, size in bytes) for lds_dma16.
+__device__ __forceinline__ u32x4 raw_rsrc(const void* base, int bytes) {
+  const uint64_t p = (uint64_t)base;
+  return u32x4{(uint32_t)p, (uint32_t)(p >> 32) & 0xffffu, (uint32_t)bytes,
+               (uint32_t)kRawBufferFlags};
+}
+
+// A 1 KiB direct-to-LDS load (lane l copies 16 bytes from buffer offset voff to LDS byte
+// lds + 16 l) and a 16-byte LDS store of zeros, written as assembly: the compiler does not see
+// them, and their ordering is left to explicit waits.
+__device__ __forceinline__ void lds_dma16(const u32x4& rsrc, uint32_t lds, int voff) {
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(rsrc), "{m0}"(lds)
+               : "memory");
+}
+__device__ __forceinline__ void lds_zero16(uint32_t lds) {
+  asm volatile("ds_write_b128 %0, %1" : : "v"(lds), "v"(u32x4{0, 0, 0, 0}) : "memory");
+}
 
 template <int D>
 struct WideWave {
@@ -491,13 +518,6 @@ __device__ __forceinline__ void wide_item_body(const FwdArgs& a, int id, bool cl
 #pragma unroll
   for (int g = 0; g < 2; ++g) {
     const int qi = qw + 32 * g + l32;
-#pragma unroll
-    for (int kk = 0; kk < G::KS; ++kk) {
-      if (qi < a.Sq)
-        w.qf[g][kk] = *reinterpret_cast<const u32x4*>(qbase + (size_t)qi * D + kk * 16 + h * 8);
-      else
-        w.qf[g][kk] = u32x4{0, 0, 0, 0};
-    }
     w.lim[g] = CAUSAL ? min(a.Sk, qi + off + 1) : a.Sk;
 #pragma unroll
     for (int i = 0; i < G::DB; ++i) w.o[g][i] = f32x16{};
@@ -518,24 +538,53 @@ __device__ __forceinline__ void wide_item_body(const FwdArgs& a, int id, bool cl
   }
   const float c = a.c;
 
-  // Every stage starts cleared: the dummy block before the first reads "V" from the second half
-  // of the last stage (0 * V must stay 0), and rows past Sk of a partial last tile are loaded
-  // out of range, which leaves finite bytes (cleared, or an earlier tile's) for masked keys.
+  // (the item's claim mark goes out first, and has returned by the wait for tile 0)
+  __shared__ int s_stolen;
+  unsigned long long took = 0;
+  if (claimed && wave == 0 && lane == 0) took = atomicMax(a.claim + kClaimHead + id, a.epoch);
+
+  // Every V stage starts cleared (stages 2 and 3 once Q has passed through them, below): the
+  // dummy block before the first reads "V" from the second half of the last stage (0 * V must
+  // stay 0), and rows past Sk of a partial tile are loaded out of range, which leaves finite V
+  // bytes (cleared, or an earlier tile's) beside the masked keys. Keys past Sk are cut out of
+  // the scores by selection, so the K stages may hold anything; each still takes a store here,
+  // ahead of every load into LDS, as do stages 2 and 3: without a store into each stage before
+  // the first such load, the compiler's tracking of these loads puts waits for loads in flight
+  // in front of reads inside the loop.
   {
 #pragma unroll
     for (int st = 0; st < kStages; ++st) {
       u32x4* kz = reinterpret_cast<u32x4*>(KS[st]);
       u32x4* vz = reinterpret_cast<u32x4*>(VS[st]);
+      kz[tid] = u32x4{0, 0, 0, 0};
 #pragma unroll
-      for (int i = 0; i < G::kTile / 16 / 256; ++i) {
-        kz[i * 256 + tid] = u32x4{0, 0, 0, 0};
+      for (int i = 0; i < (st < 2 ? G::kTile / 16 / 256 : 1); ++i)
         vz[i * 256 + tid] = u32x4{0, 0, 0, 0};
-      }
     }
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   }
+
+  // Q of the wave (its 64 rows, 16 KiB) passes through LDS, with whole rows per load (one row
+  // per lane would touch each row's 256 bytes in 16 pieces): into a quarter of stages 2 and 3,
+  // which the first tiles leave free, in the K tiles' layout, so that the fragments are read
+  // with the K operand offsets. Rows past Sq load row Sq - 1 (every tile has a row below Sq):
+  // they are computed like it, and never stored. (Written as assembly: seen by the compiler
+  // ahead of the tiles' loads into stages 2 and 3, these loads would bring back the waits.)
+  char* const qs = wave == 0 ? KS[2] : wave == 1 ? KS[3] : wave == 2 ? VS[2] : VS[3];
+  {
+    const u32x4 rq = raw_rsrc(qbase + (size_t)q0 * D, kWideBM * G::kRow);
+    const int pos = lane % G::kCPR;
+    const int rsub = lane / G::kCPR;
+#pragma unroll
+    for (int i = 0; i < kWideRows / G::kRPI; ++i) {
+      const int r = i * G::kRPI + rsub;             // row among the wave's 64
+      const int src = min(qw + r, a.Sq - 1) - q0;
+      lds_dma16(rq, lds_addr(qs) + i * 1024, src * G::kRow + ((pos ^ kswz<D>(r)) * 16));
+    }
+  }
+  static_assert(kWideRows / G::kRPI == 16, "D = 128: 16 Q loads per wave");
   TileDma<D, 4> dma;
   dma.init(wave, lane, kbase, vbase, a.Sk);
   // Loads: a wave's 8 loads of tile X go out one at a time between the matrix-core instructions
@@ -544,19 +593,43 @@ __device__ __forceinline__ void wide_item_body(const FwdArgs& a, int id, bool cl
   // loads in flight after tile T + 1's is always 8 at barrier T: a tile past the workgroup's
   // last loads, instead, the tile its stage already holds (X - 4, the same bytes), or for X < 4
   // tile X itself into a stage no tile uses. Tiles 0 and 1 and the first three loads of tile 2
-  // are issued here; then wait for tile 0 (and the Q fragments, loaded earlier).
+  // are issued here (tile 2's once Q has been read out of the stages); then wait for tile 0.
   constexpr int kParts = 2 * G::kIPW;      // loads per wave and tile
   static_assert(kParts == 8, "D = 128: 4 K and 4 V loads per wave and tile");
-  // (the item's claim mark goes out with the loads, and has returned by their wait)
-  __shared__ int s_stolen;
-  unsigned long long took = 0;
-  if (claimed && wave == 0 && lane == 0) took = atomicMax(a.claim + kClaimHead + id, a.epoch);
 #pragma unroll
-  for (int t = 0; t < 3; ++t) {
+  for (int t = 0; t < 2; ++t) {
 #pragma unroll
-    for (int j = 0; j < (t < 2 ? kParts : 3); ++j)
-      dma.issue_part_unclamped(KS[t], VS[t], kt0 + t * kBN, j);
+    for (int j = 0; j < kParts; ++j) dma.issue_part_unclamped(KS[t], VS[t], kt0 + t * kBN, j);
   }
+  // The wave's Q has landed (the tiles' 16 loads are still out). Each wave reads its fragments
+  // (its stage named in a branch of its own, so that the reads carry that stage's alias
+  // information), those holding Q in a V stage clear it, and tile 2 may overwrite stage 2 once
+  // every wave is past the barrier.
+  __builtin_amdgcn_s_waitcnt(kWaitVm16);
+  asm volatile("" ::: "memory");
+  auto q_read = [&](const char* st) {
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+#pragma unroll
+      for (int kk = 0; kk < G::KS; ++kk)
+        w.qf[g][kk] = *reinterpret_cast<const u32x4*>(st + 32 * g * G::kRow + w.koff[kk]);
+    }
+  };
+  if (wave == 0) {
+    q_read(KS[2]);
+  } else if (wave == 1) {
+    q_read(KS[3]);
+  } else {
+    q_read(wave == 2 ? VS[2] : VS[3]);
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+#pragma unroll
+    for (int i = 0; i < G::kTile / 1024; ++i) lds_zero16(lds_addr(qs) + i * 1024 + lane * 16);
+  }
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+#pragma unroll
+  for (int j = 0; j < 3; ++j) dma.issue_part_unclamped(KS[2], VS[2], kt0 + 2 * kBN, j);
   __builtin_amdgcn_s_waitcnt(kWaitVm11);
   if (claimed && wave == 0 && lane == 0) s_stolen = took == (a.epoch | 1ull);
   __builtin_amdgcn_s_waitcnt(kWaitLgkm0);

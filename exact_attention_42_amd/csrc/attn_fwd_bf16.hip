@@ -118,10 +118,6 @@ __device__ __forceinline__ void fwd_tile_body(const FwdArgs& a) {
       else
         w.qf[kk] = u32x4{0, 0, 0, 0};
     }
-    // Consume the Q loads here: otherwise the loop's first use of qf must wait for every
-    // outstanding global load, including the next tile's prefetch.
-#pragma unroll
-    for (int kk = 0; kk < G::KS; ++kk) asm volatile("" : "+v"(w.qf[kk]));
   }
 #pragma unroll
   for (int i = 0; i < G::DB; ++i) w.o[i] = f32x16{};
@@ -149,6 +145,10 @@ __device__ __forceinline__ void fwd_tile_body(const FwdArgs& a) {
   dma.init(wave, lane, kbase, vbase, a.Sk);
   if (ntiles > 0) dma.issue(sk0, sv0, t0 * kBN, a.Sk);
   wait_dma_and_barrier();
+  // Q and the first tile were in flight together. Consume the Q loads here, where they have
+  // landed: otherwise the loop's first use of qf waits for every load in flight then,
+  // including the next tile's prefetch.
+  consume_q(w);
 
   for (int j = 0; j < ntiles; j += 2) {
     const int kt = (t0 + j) * kBN;
@@ -411,6 +411,7 @@ __device__ __forceinline__ void fwd_pair_pipe_body(const FwdArgs& a) {
   }
   const float c = a.c;
 
+  // Q of 32 rows from qw (consumed by the caller: consume_q), O and the softmax state reset
   auto begin_rows = [&](int qw) {
     const int qi = qw + l32;
 #pragma unroll
@@ -420,8 +421,6 @@ __device__ __forceinline__ void fwd_pair_pipe_body(const FwdArgs& a) {
       else
         w.qf[kk] = u32x4{0, 0, 0, 0};
     }
-#pragma unroll
-    for (int kk = 0; kk < G::KS; ++kk) asm volatile("" : "+v"(w.qf[kk]));
 #pragma unroll
     for (int i = 0; i < G::DB; ++i) w.o[i] = f32x16{};
     w.mref = -INFINITY;
@@ -510,7 +509,10 @@ __device__ __forceinline__ void fwd_pair_pipe_body(const FwdArgs& a) {
     if (row_switch) {
       store_rows(qw);
       qw = qheavy;
-      if (nB > 0) begin_rows(qw);
+      if (nB > 0) {
+        begin_rows(qw);
+        consume_q(w);
+      }
     }
     if (!vis) return;
     const char* kt_lds = sb ? kbc : kac;
@@ -541,6 +543,7 @@ __device__ __forceinline__ void fwd_pair_pipe_body(const FwdArgs& a) {
   if (lwave && x > 0) dma.issue_one(false, ka0, 0, a.Sk);
   if (lwave && in_b(0)) dma.issue_one(false, kb0, ktb(0), a.Sk);
   wait_dma_and_barrier();
+  consume_q(w);   // (Q and the first K tile were in flight together)
   for (int j = 0; j <= x; j += 2) {
     dma_step(j, ka1, kb1, va0, vb0);
     step(j, ka0, kb0, va1, vb1);

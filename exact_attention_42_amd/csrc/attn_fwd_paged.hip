@@ -212,8 +212,6 @@ __device__ __forceinline__ void fwd_paged_body(const PagedArgs& a) {
         w.qf[kk] = u32x4{0, 0, 0, 0};
     }
 #pragma unroll
-    for (int kk = 0; kk < G::KS; ++kk) asm volatile("" : "+v"(w.qf[kk]));
-#pragma unroll
     for (int i = 0; i < G::DB; ++i) w.o[i] = f32x16{};
     w.mref = -INFINITY;
     w.l_run = 0.f;
@@ -233,6 +231,7 @@ __device__ __forceinline__ void fwd_paged_body(const PagedArgs& a) {
       if (ntiles > 1) ent_next = load_page_ids(trow, kt0 + kBN, nblk, lane);
     }
     wait_dma_and_barrier();
+    consume_q(w);   // (Q, the table entries and the first tile were in flight together)
 
     for (int j = 0; j < ntiles; j += 2) {
       const int kt = (t0 + j) * kBN;

@@ -181,6 +181,15 @@ struct WaveState {
   int voff[G::DB];          // per-lane V^T transposed-read offsets within a tile
 };
 
+// Marks the Q fragments as used (an empty assembly block that reads and writes them), so that
+// the compiler waits for their loads at this point and at no later one. Placed after a wait
+// for all loads in flight, it costs nothing.
+template <int D>
+__device__ __forceinline__ void consume_q(WaveState<D>& w) {
+#pragma unroll
+  for (int kk = 0; kk < Geo<D, 4>::KS; ++kk) asm volatile("" : "+v"(w.qf[kk]));
+}
+
 // max / sum of x over lanes l and l ^ 32. v_permlane32_swap returns the low half of x in
 // both halves of one register and the high half in both halves of the other, so the pair
 // (l, l ^ 32) meets in every lane with no LDS round trip.

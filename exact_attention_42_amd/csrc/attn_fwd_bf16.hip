@@ -411,8 +411,15 @@ __device__ __forceinline__ void fwd_pair_pipe_body(const FwdArgs& a) {
   }
   const float c = a.c;
 
-  // Q of 32 rows from qw (consumed by the caller: consume_q), O and the softmax state reset
-  auto begin_rows = [&](int qw) {
+  // O and the softmax state reset for new rows
+  auto reset_rows = [&]() {
+#pragma unroll
+    for (int i = 0; i < G::DB; ++i) w.o[i] = f32x16{};
+    w.mref = -INFINITY;
+    w.l_run = 0.f;
+  };
+  // Q of 32 rows from qw straight into the fragments (one row per lane; rows past Sq zero)
+  auto load_q = [&](int qw) {
     const int qi = qw + l32;
 #pragma unroll
     for (int kk = 0; kk < G::KS; ++kk) {
@@ -421,10 +428,6 @@ __device__ __forceinline__ void fwd_pair_pipe_body(const FwdArgs& a) {
       else
         w.qf[kk] = u32x4{0, 0, 0, 0};
     }
-#pragma unroll
-    for (int i = 0; i < G::DB; ++i) w.o[i] = f32x16{};
-    w.mref = -INFINITY;
-    w.l_run = 0.f;
   };
   auto store_rows = [&](int qw) {
     const int my_q = qw + l32;
@@ -445,15 +448,37 @@ __device__ __forceinline__ void fwd_pair_pipe_body(const FwdArgs& a) {
   int qw;
   if (lwave && !single) {
     qw = qlight;
-    begin_rows(qw);
+    reset_rows();
     if (nL == 0) {
       store_rows(qw);
       qw = qheavy;
-      begin_rows(qw);
+      reset_rows();
     }
   } else {
     qw = qheavy;
-    begin_rows(qw);
+    reset_rows();
+  }
+  // The first rows' Q passes through LDS, with whole rows per load (one row per lane would
+  // touch each row's bytes in 32-byte pieces): wave w's 32 rows go to half w % 2 of the V stage
+  // of steps 0 and 1 (va0, vb0, va1, vb1 for w / 2 = 0..3), which no load uses before the loop,
+  // in the K tiles' layout, so that the fragments are read with the K operand offsets. Rows
+  // past Sq load row Sq - 1: they are computed like it, and never stored. (The loads are
+  // assembly, which the compiler does not track: the wait before the loop covers them.)
+  constexpr int kQBytes = 32 * G::kRow;
+  static_assert(2 * kQBytes == G::kTile, "two waves' rows per stage");
+  {
+    char* const qs = (wave < 2 ? va0 : wave < 4 ? vb0 : wave < 6 ? va1 : vb1) +
+                     (wave & 1) * kQBytes;
+    const int rb = min(qw, a.Sq - 1);               // first row loaded
+    const u32x4 rq = raw_rsrc(qbase + (size_t)rb * D, kQBytes);
+    const int pos = lane % G::kCPR;
+    const int rsub = lane / G::kCPR;
+#pragma unroll
+    for (int i = 0; i < kQBytes / 1024; ++i) {
+      const int r = i * G::kRPI + rsub;             // row among the wave's 32
+      const int src = min(qw + r, a.Sq - 1) - rb;
+      lds_dma16(rq, lds_addr(qs) + i * 1024, src * G::kRow + ((pos ^ kswz<D>(r)) * 16));
+    }
   }
 
   Pipe<D> p;
@@ -510,7 +535,8 @@ __device__ __forceinline__ void fwd_pair_pipe_body(const FwdArgs& a) {
       store_rows(qw);
       qw = qheavy;
       if (nB > 0) {
-        begin_rows(qw);
+        reset_rows();
+        load_q(qw);
         consume_q(w);
       }
     }
@@ -543,7 +569,22 @@ __device__ __forceinline__ void fwd_pair_pipe_body(const FwdArgs& a) {
   if (lwave && x > 0) dma.issue_one(false, ka0, 0, a.Sk);
   if (lwave && in_b(0)) dma.issue_one(false, kb0, ktb(0), a.Sk);
   wait_dma_and_barrier();
-  consume_q(w);   // (Q and the first K tile were in flight together)
+  // Q and the first K tile were in flight together. Each wave reads its fragments (its stage
+  // named in a branch of its own, so that the reads carry that stage's alias information);
+  // the loop's first loads overwrite va0 and vb0 once every wave is past the barrier.
+  {
+    auto q_read = [&](const char* st) {
+#pragma unroll
+      for (int kk = 0; kk < G::KS; ++kk)
+        w.qf[kk] = *reinterpret_cast<const u32x4*>(st + (wave & 1) * kQBytes + w.koff[kk]);
+    };
+    if (wave < 2) q_read(va0);
+    else if (wave < 4) q_read(vb0);
+    else if (wave < 6) q_read(va1);
+    else q_read(vb1);
+    consume_q(w);
+    __syncthreads();
+  }
   for (int j = 0; j <= x; j += 2) {
     dma_step(j, ka1, kb1, va0, vb0);
     step(j, ka0, kb0, va1, vb1);

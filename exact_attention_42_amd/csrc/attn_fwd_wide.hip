@@ -65,32 +65,6 @@ constexpr int kWaitVm8 = 0x0F78;
 constexpr int kWaitVm11 = 0x0F7B;
 constexpr int kWaitVm16 = 0x4F70;   // (vmcnt's two high bits sit at 15:14)
 
-typedef __attribute__((address_space(3))) char lds_char;
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const lds_char*)p;
-}
-
-// Raw buffer descriptor (base, no stride, size in bytes) for lds_dma16.
-__device__ __forceinline__ u32x4 raw_rsrc(const void* base, int bytes) {
-  const uint64_t p = (uint64_t)base;
-  return u32x4{(uint32_t)p, (uint32_t)(p >> 32) & 0xffffu, (uint32_t)bytes,
-               (uint32_t)kRawBufferFlags};
-}
-
-// A 1 KiB direct-to-LDS load (lane l copies 16 bytes from buffer offset voff to LDS byte
-// lds + 16 l) and a 16-byte LDS store of zeros, written as assembly: the compiler does not see
-// them, and their ordering is left to explicit waits.
-__device__ __forceinline__ void lds_dma16(const u32x4& rsrc, uint32_t lds, int voff) {
-  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
-               :
-               : "v"(voff), "s"(rsrc), "{m0}"(lds)
-               : "memory");
-}
-__device__ __forceinline__ void lds_zero16(uint32_t lds) {
-  asm volatile("ds_write_b128 %0, %1" : : "v"(lds), "v"(u32x4{0, 0, 0, 0}) : "memory");
-}
-
 template <int D>
 struct WideWave {
   using G = Geo<D, 4>;

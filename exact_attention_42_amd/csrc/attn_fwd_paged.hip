@@ -188,6 +188,14 @@ __device__ __forceinline__ void fwd_paged_body(const PagedArgs& a) {
   }
   const float c = a.c;
 
+  constexpr int kQBytes = 32 * G::kRow;             // Q of one wave's rows
+  static_assert(2 * kQBytes == G::kTile, "two waves' rows per tile");
+  auto q_read = [&](const char* st) {
+#pragma unroll
+    for (int kk = 0; kk < G::KS; ++kk)
+      w.qf[kk] = *reinterpret_cast<const u32x4*>(st + (wave & 1) * kQBytes + w.koff[kk]);
+  };
+
   // Every rank of this sequence that the grid leaves over (the grid has a.ntq ranks; a
   // sequence with more query tiles wraps around) is done by the workgroups of the first ranks.
   for (int rank = rank0; rank < ntq_b; rank += a.ntq) {
@@ -203,13 +211,25 @@ __device__ __forceinline__ void fwd_paged_body(const PagedArgs& a) {
     const int t0 = SPLIT ? split * nall / a.nsplit : 0;
     const int ntiles = SPLIT ? (split + 1) * nall / a.nsplit - t0 : nall;
 
+    // Q of the wave's 32 rows passes through LDS, with whole rows per load (one row per lane
+    // would touch each row's bytes in 32-byte pieces): wave w's rows go to half w % 2 of stage
+    // 1's K (w < 2) or V tile, which the loop first loads into after the barrier below, in the
+    // K tiles' layout, so that the fragments are read with the K operand offsets. Rows past Sq
+    // load row Sq - 1: they are computed like it, and never stored. (The loads are assembly,
+    // which the compiler does not track: the wait for the first tile covers them. They take
+    // per-lane addresses: a token's rows are Hq * D elements apart, more than a buffer offset
+    // spans for large Hq.)
+    {
+      char* const qst = (wave < 2 ? sk1 : sv1) + (wave & 1) * kQBytes;
+      const int pos = lane % G::kCPR;
+      const int rsub = lane / G::kCPR;
 #pragma unroll
-    for (int kk = 0; kk < G::KS; ++kk) {
-      if (my_q < Sq)
-        w.qf[kk] = *reinterpret_cast<const u32x4*>(
-            a.q + ((size_t)(qs + my_q) * a.Hq + hq) * D + kk * 16 + h * 8);
-      else
-        w.qf[kk] = u32x4{0, 0, 0, 0};
+      for (int i = 0; i < kQBytes / 1024; ++i) {
+        const int r = i * G::kRPI + rsub;             // row among the wave's 32
+        const int t = qs + min(qw + r, Sq - 1);       // its token
+        lds_dma16_global(a.q + ((size_t)t * a.Hq + hq) * D + (pos ^ kswz<D>(r)) * 8,
+                         lds_addr(qst) + i * 1024);
+      }
     }
 #pragma unroll
     for (int i = 0; i < G::DB; ++i) w.o[i] = f32x16{};
@@ -231,7 +251,21 @@ __device__ __forceinline__ void fwd_paged_body(const PagedArgs& a) {
       if (ntiles > 1) ent_next = load_page_ids(trow, kt0 + kBN, nblk, lane);
     }
     wait_dma_and_barrier();
-    consume_q(w);   // (Q, the table entries and the first tile were in flight together)
+    // Q, the table entries and the first tile were in flight together. Each wave reads its
+    // fragments (its stage named in a branch of its own, so that the reads carry that stage's
+    // alias information); the waves that held Q in the V tile clear it again (a masked key
+    // must find finite bytes there); the loop first loads into stage 1 after the barrier.
+    if (wave < 2) {
+      q_read(sk1);
+    } else {
+      q_read(sv1);
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+#pragma unroll
+      for (int i = 0; i < kQBytes / 1024; ++i)
+        lds_zero16(lds_addr(sv1 + (wave & 1) * kQBytes) + i * 1024 + lane * 16);
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    __syncthreads();
 
     for (int j = 0; j < ntiles; j += 2) {
       const int kt = (t0 + j) * kBN;

@@ -204,9 +204,6 @@ __device__ __forceinline__ void stretch_pattern_early_ds() {
   }
 }
 
-// s_waitcnt immediate: lgkmcnt(0), vmcnt and expcnt left free
-constexpr int kWaitLgkm0 = 0xC07F;
-
 // Issue pattern of one stretch of 8 matrix-core instructions: after each one, DS LDS reads,
 // T transcendental (exponential) and V other vector instructions. (Sched-group masks: 0x008
 // matrix core, 0x100 LDS read, 0x400 transcendental, 0x002 vector ALU.)

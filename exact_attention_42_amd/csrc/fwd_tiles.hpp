@@ -65,6 +65,9 @@ struct FwdArgs {
 // Buffer resource word 3 for raw (untyped) loads on gfx9-family parts.
 constexpr int kRawBufferFlags = 0x00020000;
 
+// s_waitcnt immediate: lgkmcnt(0), vmcnt and expcnt left free
+constexpr int kWaitLgkm0 = 0xC07F;
+
 typedef __attribute__((address_space(3))) char lds_char;
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -86,6 +89,11 @@ __device__ __forceinline__ void lds_dma16(const u32x4& rsrc, uint32_t lds, int v
                :
                : "v"(voff), "s"(rsrc), "{m0}"(lds)
                : "memory");
+}
+// The same load from per-lane 64-bit addresses: lane l copies the 16 bytes at src to LDS byte
+// lds + 16 l.
+__device__ __forceinline__ void lds_dma16_global(const void* src, uint32_t lds) {
+  asm volatile("global_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(lds) : "memory");
 }
 __device__ __forceinline__ void lds_zero16(uint32_t lds) {
   asm volatile("ds_write_b128 %0, %1" : : "v"(lds), "v"(u32x4{0, 0, 0, 0}) : "memory");

@@ -19,6 +19,10 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libattn.so")
+# The same library with every kernel's LDS filled with NaN bytes before use (-DATTN_POISON_LDS):
+# a check build whose results must equal libattn.so's bit for bit. Only the tests load it.
+LIB_POISON = os.path.join(PKG, "libattn_poison.so")
+POISON_FLAGS = ("-DATTN_POISON_LDS",)
 ARCH = "gfx950"
 
 # -packed-fp32-ops: keep the compiler from forming packed fp32 VALU instructions.
@@ -83,6 +87,13 @@ def build(verbose: bool = False, extra_flags=(), out: str = LIB) -> str:
     return out
 
 
+def build_all(verbose: bool = False) -> None:
+    """libattn.so, then the LDS-poisoning check build next to it."""
+    build(verbose)
+    build(verbose, extra_flags=POISON_FLAGS, out=LIB_POISON)
+
+
 if __name__ == "__main__":
-    path = build(verbose="-v" in sys.argv)
-    print(path)
+    build_all(verbose="-v" in sys.argv)
+    print(LIB)
+    print(LIB_POISON)

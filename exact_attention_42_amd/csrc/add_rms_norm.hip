@@ -50,6 +50,8 @@ __device__ __forceinline__ u32x4 narrow8(const float (&f)[8]) {
 template <int VPT>
 __global__ __launch_bounds__(kNormMaxThreads) void add_rms_norm_kernel(NormArgs a) {
   __shared__ float part[kNormMaxThreads / 64];
+  lds_poison(part, sizeof(part));
+  lds_poison_done();
   const int T = blockDim.x;
   const int tid = threadIdx.x;
   const size_t row = (size_t)blockIdx.x * a.d;

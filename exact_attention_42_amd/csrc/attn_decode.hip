@@ -175,6 +175,8 @@ __attribute__((amdgpu_waves_per_eu(ATTN_DEC_WAVES_PER_EU))) void decode_stream_k
   constexpr int KS = D / 32;        // 16x16x32 k-steps of the score product
   constexpr int DT = D / 16;        // 16-row d tiles of O^T
   __shared__ __attribute__((aligned(1024))) char smem[kDecWaves * NS * G::kSlot];
+  lds_poison(smem, sizeof(smem));
+  lds_poison_done();
 
   const int lane = threadIdx.x & 63;
   const int wave = wave_uniform(threadIdx.x >> 6);   // scalar: block addresses are per wave

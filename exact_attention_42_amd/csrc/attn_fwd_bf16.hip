@@ -74,6 +74,11 @@ __device__ __forceinline__ void fwd_tile_body(const FwdArgs& a) {
   __shared__ __attribute__((aligned(1024))) char sv0[G::kTile];
   __shared__ __attribute__((aligned(1024))) char sk1[G::kTile];
   __shared__ __attribute__((aligned(1024))) char sv1[G::kTile];
+  lds_poison(sk0, G::kTile);
+  lds_poison(sv0, G::kTile);
+  lds_poison(sk1, G::kTile);
+  lds_poison(sv1, G::kTile);
+  lds_poison_done();
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -353,6 +358,13 @@ __device__ __forceinline__ void fwd_pair_pipe_body(const FwdArgs& a) {
   __shared__ __attribute__((aligned(1024))) char kb1[G::kTile];
   __shared__ __attribute__((aligned(1024))) char vb1[G::kTile];
   __shared__ float xml[4][2][64];     // hand-over of (mref, l_run) from the L waves
+  {
+    char* const st[8] = {ka0, va0, ka1, va1, kb0, vb0, kb1, vb1};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) lds_poison(st[i], G::kTile);
+    lds_poison(xml, sizeof(xml));
+    lds_poison_done();
+  }
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;

@@ -34,6 +34,9 @@ __global__ __launch_bounds__(kThreadsF) void fwd_f32_kernel(FwdF32Args a) {
   constexpr int QPB = kThreadsF / TPQ;        // queries per workgroup
   __shared__ float ks[kTileF][D];
   __shared__ float vs[kTileF][D];
+  lds_poison(ks, sizeof(ks));
+  lds_poison(vs, sizeof(vs));
+  lds_poison_done();
 
   const int tid = threadIdx.x;
   const int part = tid % TPQ;

@@ -127,6 +127,11 @@ __device__ __forceinline__ void fwd_paged_body(const PagedArgs& a) {
   __shared__ __attribute__((aligned(1024))) char sv0[G::kTile];
   __shared__ __attribute__((aligned(1024))) char sk1[G::kTile];
   __shared__ __attribute__((aligned(1024))) char sv1[G::kTile];
+  lds_poison(sk0, G::kTile);
+  lds_poison(sv0, G::kTile);
+  lds_poison(sk1, G::kTile);
+  lds_poison(sv1, G::kTile);
+  lds_poison_done();
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;

@@ -432,6 +432,12 @@ __device__ __forceinline__ void wide_item_body(const FwdArgs& a, int id, bool cl
   __shared__ __attribute__((aligned(1024))) char b_k3[G::kTile];
   char* const KS[kStages] = {b_k0, b_k1, b_k2, b_k3};
   char* const VS[kStages] = {a_v0, a_v1, a_v2, a_v3};
+#pragma unroll
+  for (int st = 0; st < kStages; ++st) {
+    lds_poison(KS[st], G::kTile);
+    lds_poison(VS[st], G::kTile);
+  }
+  lds_poison_done();
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;

@@ -92,4 +92,18 @@ __device__ __forceinline__ void wave_lds_fence() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Debug builds (-DATTN_POISON_LDS): a kernel first fills the LDS arrays it uses with 0xff bytes
+// (NaN as fp32 and as bf16), then synchronises the workgroup, so that reading any LDS byte the
+// kernel has not written itself shows in its results. In normal builds both calls are empty.
+#ifdef ATTN_POISON_LDS
+__device__ __forceinline__ void lds_poison(void* p, size_t bytes) {
+  uint32_t* w = static_cast<uint32_t*>(p);
+  for (size_t i = threadIdx.x; i < bytes / 4; i += blockDim.x) w[i] = 0xffffffffu;
+}
+__device__ __forceinline__ void lds_poison_done() { __syncthreads(); }
+#else
+__device__ __forceinline__ void lds_poison(void*, size_t) {}
+__device__ __forceinline__ void lds_poison_done() {}
+#endif
+
 }  // namespace cdna4

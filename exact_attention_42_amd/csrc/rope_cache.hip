@@ -58,6 +58,9 @@ __global__ __launch_bounds__(kRopeThreads) void rope_cache_kernel(RopeArgs a) {
   constexpr int H2 = D / 2;          // rotation pairs
   constexpr int VP = D / 16;         // vector pairs per head
   __shared__ float cs[H2], sn[H2];
+  lds_poison(cs, sizeof(cs));
+  lds_poison(sn, sizeof(sn));
+  lds_poison_done();
   const int t = blockIdx.x;
   const int tid = threadIdx.x;
   const int p = a.pos[t];

@@ -265,6 +265,18 @@ def test_library_defines_every_kernel_launch_stub():
     assert undefined == []
 
 
+def test_check_build_exports_the_same_symbols():
+    """libattn_poison.so, the LDS-poisoning check build that the GPU tests compare with
+    libattn.so, is built beside it from the same sources: it exports every declared symbol and
+    misses no kernel launch stub."""
+    path = os.path.join(os.path.dirname(A.library_path()), "libattn_poison.so")
+    assert os.path.exists(path), f"{path} is missing: run __graft_entry__.build()"
+    out = subprocess.run(["nm", "-D", path], capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (attn_\w+)$", out, flags=re.M))
+    assert set(header_functions()) <= exported
+    assert [l for l in out.splitlines() if " U " in l and "device_stub" in l] == []
+
+
 def norm(*, x=P, r=P, w=P, o=P, t=P, M=4, d=4096, eps=1e-6):
     return A.load_library().attn_add_rms_norm(x, r, w, o, t, M, d, eps, None)
 

@@ -412,6 +412,54 @@ __device__ __forceinline__ void wide_item(int id, int nitems, int ntq, int group
   bh = kvh * group + (r - rank * group);
 }
 
+// The epilogue writes O through LDS so that every store instruction covers whole rows. Stored
+// straight from the accumulators (store_o_group), one instruction writes 32 bytes into each of
+// 32 rows, four times as many partial-line writes as the same bytes in whole rows.
+//
+// stage_o_group: normalised O of one 32-row group into the wave's LDS region, one row per
+// query (G::kRow bytes, 16-byte chunk c of row r at slot c ^ kswz(r)). The lane's chunks are
+// formed as in store_o_group: after the half swap, lane (l32, h) holds chunks 4 db + 2 k + h of
+// row row0 + l32.
+template <int D>
+__device__ __forceinline__ void stage_o_group(char* st, int row0, const f32x16 (&o)[D / 32],
+                                              float inv, int h, int l32) {
+  using G = Geo<D, 4>;
+  int r = row0 + l32;
+  asm volatile("" : "+v"(r), "+v"(h));   // (addresses formed here, not hoisted above the loop)
+#pragma unroll
+  for (int db = 0; db < G::DB; ++db)
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int e0 = 2 * k, e1 = 2 * k + 1;
+      const uint32_t x0 = pack_bf16x2(o[db][4 * e0 + 0] * inv, o[db][4 * e0 + 1] * inv);
+      const uint32_t x1 = pack_bf16x2(o[db][4 * e0 + 2] * inv, o[db][4 * e0 + 3] * inv);
+      const uint32_t y0 = pack_bf16x2(o[db][4 * e1 + 0] * inv, o[db][4 * e1 + 1] * inv);
+      const uint32_t y1 = pack_bf16x2(o[db][4 * e1 + 2] * inv, o[db][4 * e1 + 3] * inv);
+      const auto s0 = __builtin_amdgcn_permlane32_swap(x0, y0, false, false);
+      const auto s1 = __builtin_amdgcn_permlane32_swap(x1, y1, false, false);
+      const int ch = 4 * db + 2 * k + h;
+      *reinterpret_cast<u32x4*>(st + r * G::kRow + ((ch ^ kswz<D>(r)) * 16)) =
+          u32x4{s0[0], s1[0], s0[1], s1[1]};
+    }
+}
+// store_staged_rows: the wave's kWideRows staged rows back out, G::kCPR lanes per row, so that
+// one store covers 64 / kCPR consecutive rows (1 KiB at D = 128). Rows from `nvalid` on are
+// not stored.
+template <int D>
+__device__ __forceinline__ void store_staged_rows(uint16_t* obase, const char* st, int nvalid,
+                                                  int lane) {
+  using G = Geo<D, 4>;
+  constexpr int kRowsPerStore = 64 / G::kCPR;
+  asm volatile("" : "+v"(lane));         // (addresses formed here, not hoisted above the loop)
+  const int cc = lane % G::kCPR;
+#pragma unroll
+  for (int i = 0; i < kWideRows / kRowsPerStore; ++i) {
+    const int r = kRowsPerStore * i + lane / G::kCPR;
+    const u32x4 x = *reinterpret_cast<const u32x4*>(st + r * G::kRow + ((cc ^ kswz<D>(r)) * 16));
+    if (r < nvalid) *reinterpret_cast<u32x4*>(obase + (size_t)r * D + cc * 8) = x;
+  }
+}
+
 // One work item on the workgroup. SPLIT: the workgroup covers one of a.nsplit contiguous ranges
 // of its query tile's key tiles and writes that range's own output (bf16, normalised by the
 // range's sum), reference max and sum to the workspace; a merge kernel combines the ranges
@@ -707,38 +755,44 @@ __device__ __forceinline__ void wide_item_body(const FwdArgs& a, int id, bool cl
   }
   __builtin_amdgcn_s_waitcnt(kWaitVm0);   // (no load may still be writing LDS at the end)
 
+  // ---- epilogue: normalise O and stage it as rows in the wave's K stage (at the barrier every
+  //      wave is past its last read of the K stages, and every load has landed), then store
+  //      whole rows ----
+  static_assert(kWideRows * G::kRow == G::kTile, "a wave's rows of O fill one K stage");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  char* const os = wave == 0 ? KS[0] : wave == 1 ? KS[1] : wave == 2 ? KS[2] : KS[3];
+  float l_tot[2];
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    l_tot[g] = xor32_sum(w.l[g]);
+    stage_o_group<D>(os, 32 * g, w.o[g], (l_tot[g] > 0.f) ? 1.f / l_tot[g] : 0.f, h, l32);
+  }
+  const int nvalid = min(kWideRows, a.Sq - qw);
   if (SPLIT) {
     // ---- partial result: this key range's own output (bf16), reference max (base 2,
     //      scaled) and sum ----
-    const size_t nrows = (size_t)a.B * a.Hq * a.Sq;
+    const size_t prow0 =
+        (size_t)split * a.B * a.Hq * a.Sq + (size_t)(b * a.Hq + hq) * a.Sq + qw;
+    store_staged_rows<D>(a.part_o + prow0 * D, os, nvalid, lane);
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
-      const int my_q = qw + 32 * g + l32;
-      const float l_tot = xor32_sum(w.l[g]);
-      const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
-      const size_t prow =
-          (size_t)split * nrows + (size_t)(b * a.Hq + hq) * a.Sq + min(my_q, a.Sq - 1);
-      store_o_group<G::DB>(a.part_o + prow * D, w.o[g], inv, h, my_q < a.Sq);
-      if (my_q < a.Sq && h == 0)
-        *reinterpret_cast<f32x2*>(a.part_ml + prow * 2) =
-            f32x2{l_tot > 0.f ? w.m[g] : -INFINITY, l_tot};
+      const int r = 32 * g + l32;
+      if (r < nvalid && h == 0)
+        *reinterpret_cast<f32x2*>(a.part_ml + (prow0 + r) * 2) =
+            f32x2{l_tot[g] > 0.f ? w.m[g] : -INFINITY, l_tot[g]};
     }
     return;
   }
-
-  // ---- epilogue: normalise, store O (bf16) and LSE (natural log) ----
+  const size_t orow0 = (size_t)(b * a.Hq + hq) * a.Sq + qw;
+  store_staged_rows<D>(a.o + orow0 * D, os, nvalid, lane);
+  // LSE (natural log)
 #pragma unroll
   for (int g = 0; g < 2; ++g) {
-    const int my_q = qw + 32 * g + l32;
-    const float l_tot = xor32_sum(w.l[g]);
-    const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
-    store_o_group<G::DB>(a.o + ((size_t)(b * a.Hq + hq) * a.Sq + min(my_q, a.Sq - 1)) * D,
-                         w.o[g], inv, h, my_q < a.Sq);
-    if (my_q < a.Sq) {
-      if (a.lse != nullptr && h == 0) {
-        const float lse = (l_tot > 0.f) ? (w.m[g] + log2_fast(l_tot)) * kLn2 : -INFINITY;
-        a.lse[(size_t)(b * a.Hq + hq) * a.Sq + my_q] = lse;
-      }
+    const int r = 32 * g + l32;
+    if (r < nvalid && a.lse != nullptr && h == 0) {
+      const float lse = (l_tot[g] > 0.f) ? (w.m[g] + log2_fast(l_tot[g])) * kLn2 : -INFINITY;
+      a.lse[orow0 + r] = lse;
     }
   }
 }

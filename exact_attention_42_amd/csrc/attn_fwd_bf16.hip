@@ -632,7 +632,18 @@ __device__ __forceinline__ void fwd_pair_pipe_body(const FwdArgs& a) {
           w.o[db][r] = w.o[db][r] * a1 + xo[(16 * db + r) * 64 + lane] * a2;
     }
   }
-  if (!lwave) store_rows(qw);
+  if (!lwave) {
+    // the heavy rows leave through LDS as whole rows (stage_o_group), each wave's through the
+    // stage it took the hand-over in, which no other wave reads; the loop ended with a barrier,
+    // so no wave reads a stage any more and no load is writing one
+    char* const os = wr == 0 ? ka0 : wr == 1 ? va0 : wr == 2 ? ka1 : va1;
+    const float l_tot = xor32_sum(w.l_run);
+    stage_o_group<D>(os, 0, w.o, (l_tot > 0.f) ? 1.f / l_tot : 0.f, h, l32);
+    const size_t orow0 = (size_t)(b * a.Hq + hq) * a.Sq + qw;
+    store_staged_rows<D, 32>(a.o + orow0 * D, os, a.Sq - qw, lane);
+    if (qw + l32 < a.Sq && a.lse != nullptr && h == 0)
+      a.lse[orow0 + l32] = (l_tot > 0.f) ? (w.mref + log2_fast(l_tot)) * kLn2 : -INFINITY;
+  }
 }
 
 template <int D, bool CAUSAL>

@@ -267,6 +267,55 @@ __device__ __forceinline__ void store_o_group(uint16_t* orow, const f32x16 (&o)[
     }
 }
 
+// O through LDS, so that every store instruction covers whole rows. Stored straight from the
+// accumulators (store_o_group), one instruction writes 32 bytes into each of 32 rows: four
+// times as many partial-line writes as the same bytes in whole rows.
+//
+// stage_o_group: normalised O of one 32-row group into the wave's LDS region, one row per
+// query (G::kRow bytes, 16-byte chunk c of row r at slot c ^ kswz(r)). The lane's chunks are
+// formed as in store_o_group: after the half swap, lane (l32, h) holds chunks 4 db + 2 k + h of
+// row row0 + l32.
+template <int D>
+__device__ __forceinline__ void stage_o_group(char* st, int row0, const f32x16 (&o)[D / 32],
+                                              float inv, int h, int l32) {
+  using G = Geo<D, 4>;
+  int r = row0 + l32;
+  asm volatile("" : "+v"(r), "+v"(h));   // (addresses formed here, not hoisted above the loop)
+#pragma unroll
+  for (int db = 0; db < G::DB; ++db)
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int e0 = 2 * k, e1 = 2 * k + 1;
+      const uint32_t x0 = pack_bf16x2(o[db][4 * e0 + 0] * inv, o[db][4 * e0 + 1] * inv);
+      const uint32_t x1 = pack_bf16x2(o[db][4 * e0 + 2] * inv, o[db][4 * e0 + 3] * inv);
+      const uint32_t y0 = pack_bf16x2(o[db][4 * e1 + 0] * inv, o[db][4 * e1 + 1] * inv);
+      const uint32_t y1 = pack_bf16x2(o[db][4 * e1 + 2] * inv, o[db][4 * e1 + 3] * inv);
+      const auto s0 = __builtin_amdgcn_permlane32_swap(x0, y0, false, false);
+      const auto s1 = __builtin_amdgcn_permlane32_swap(x1, y1, false, false);
+      const int ch = 4 * db + 2 * k + h;
+      *reinterpret_cast<u32x4*>(st + r * G::kRow + ((ch ^ kswz<D>(r)) * 16)) =
+          u32x4{s0[0], s1[0], s0[1], s1[1]};
+    }
+}
+// store_staged_rows: the wave's NROWS staged rows back out, G::kCPR lanes per row, so that one
+// store covers 64 / kCPR consecutive rows (1 KiB at D = 128). Rows from `nvalid` on are not
+// stored.
+template <int D, int NROWS>
+__device__ __forceinline__ void store_staged_rows(uint16_t* obase, const char* st, int nvalid,
+                                                  int lane) {
+  using G = Geo<D, 4>;
+  static_assert(NROWS % (64 / G::kCPR) == 0, "whole stores");
+  constexpr int kRowsPerStore = 64 / G::kCPR;
+  asm volatile("" : "+v"(lane));         // (addresses formed here, not hoisted above the loop)
+  const int cc = lane % G::kCPR;
+#pragma unroll
+  for (int i = 0; i < NROWS / kRowsPerStore; ++i) {
+    const int r = kRowsPerStore * i + lane / G::kCPR;
+    const u32x4 x = *reinterpret_cast<const u32x4*>(st + r * G::kRow + ((cc ^ kswz<D>(r)) * 16));
+    if (r < nvalid) *reinterpret_cast<u32x4*>(obase + (size_t)r * D + cc * 8) = x;
+  }
+}
+
 // Work item -> (batch, query head, pair). Workgroups are dispatched to the 8 XCDs round
 // robin; this gives XCD x a contiguous run of items, so the items of one KV head (adjacent
 // query heads of one batch) share that XCD's L2.

@@ -20,7 +20,7 @@ describes in its third paragraph: the full score row is formed, a softmax is tak
 and the probabilities weight the value vectors. Everything is done in float64 on values
 that arrive as float32 (bfloat16-exact for the bf16 workloads), so the only rounding is fp64's.
 
-Readings where the pages are silent (each also listed in the design doc):
+Readings where the pages are silent:
   * mask: none, or causal aligned to the bottom-right corner -- key j is visible to query i
     iff j <= i + (Sk - Sq); identical to the usual top-left rule when Sq == Sk;
   * a row with no visible key has O = 0 and LSE = -inf;

@@ -640,7 +640,7 @@ __device__ __forceinline__ void fwd_pair_pipe_body(const FwdArgs& a) {
     const float l_tot = xor32_sum(w.l_run);
     stage_o_group<D>(os, 0, w.o, (l_tot > 0.f) ? 1.f / l_tot : 0.f, h, l32);
     const size_t orow0 = (size_t)(b * a.Hq + hq) * a.Sq + qw;
-    store_staged_rows<D, 32>(a.o + orow0 * D, os, a.Sq - qw, lane);
+    store_staged_rows<D, 32>(a.o + orow0 * D, D, os, a.Sq - qw, lane);
     if (qw + l32 < a.Sq && a.lse != nullptr && h == 0)
       a.lse[orow0 + l32] = (l_tot > 0.f) ? (w.mref + log2_fast(l_tot)) * kLn2 : -INFINITY;
   }

@@ -303,20 +303,27 @@ __device__ __forceinline__ void fwd_paged_body(const PagedArgs& a) {
 
     const float l_tot = xor32_sum(w.l_run);
     const size_t row = (size_t)(qs + min(my_q, Sq - 1)) * a.Hq + hq;   // (Sq >= 1 here)
+    // O leaves through LDS as whole rows (stage_o_group): wave w's 32 rows go to half w % 2 of
+    // stage 0's (w < 2) or stage 1's K tile. The loop ended with a barrier, so no wave reads a
+    // stage any more and no load is writing one.
+    char* const os = (wave < 2 ? sk0 : sk1) + (wave & 1) * kQBytes;
+    stage_o_group<D>(os, 0, w.o, (l_tot > 0.f) ? 1.f / l_tot : 0.f, h, l32);
+    const size_t row0 = (size_t)(qs + qw) * a.Hq + hq;   // (an address only when qw >= Sq)
+    const size_t stride = (size_t)a.Hq * D;              // (tokens are Hq rows apart)
     if (SPLIT) {
       // this key range's own output (bf16), reference max (base 2, scaled) and sum
-      const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
-      const size_t prow = (size_t)split * R + row;
-      store_o_group<G::DB>(a.part_o + prow * D, w.o, inv, h, my_q < Sq);
+      store_staged_rows<D, 32>(a.part_o + ((size_t)split * R + row0) * D, stride, os, Sq - qw,
+                               lane);
       if (my_q < Sq && h == 0)
-        *reinterpret_cast<f32x2*>(a.part_ml + prow * 2) =
+        *reinterpret_cast<f32x2*>(a.part_ml + ((size_t)split * R + row) * 2) =
             f32x2{l_tot > 0.f ? w.mref : -INFINITY, l_tot};
     } else {
-      const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
-      store_o_group<G::DB>(a.o + row * D, w.o, inv, h, my_q < Sq);
+      store_staged_rows<D, 32>(a.o + row0 * D, stride, os, Sq - qw, lane);
       if (my_q < Sq && a.lse != nullptr && h == 0)
         a.lse[row] = (l_tot > 0.f) ? (w.mref + log2_fast(l_tot)) * kLn2 : -INFINITY;
     }
+    // (the next rank's first loads go into the stages that held O)
+    if (rank + a.ntq < ntq_b) __syncthreads();
   }
 }
 

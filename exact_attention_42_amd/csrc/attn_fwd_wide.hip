@@ -726,7 +726,7 @@ __device__ __forceinline__ void wide_item_body(const FwdArgs& a, int id, bool cl
     //      scaled) and sum ----
     const size_t prow0 =
         (size_t)split * a.B * a.Hq * a.Sq + (size_t)(b * a.Hq + hq) * a.Sq + qw;
-    store_staged_rows<D, kWideRows>(a.part_o + prow0 * D, os, nvalid, lane);
+    store_staged_rows<D, kWideRows>(a.part_o + prow0 * D, D, os, nvalid, lane);
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
       const int r = 32 * g + l32;
@@ -737,7 +737,7 @@ __device__ __forceinline__ void wide_item_body(const FwdArgs& a, int id, bool cl
     return;
   }
   const size_t orow0 = (size_t)(b * a.Hq + hq) * a.Sq + qw;
-  store_staged_rows<D, kWideRows>(a.o + orow0 * D, os, nvalid, lane);
+  store_staged_rows<D, kWideRows>(a.o + orow0 * D, D, os, nvalid, lane);
   // LSE (natural log)
 #pragma unroll
   for (int g = 0; g < 2; ++g) {

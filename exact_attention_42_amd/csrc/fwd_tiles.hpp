@@ -298,11 +298,11 @@ __device__ __forceinline__ void stage_o_group(char* st, int row0, const f32x16 (
     }
 }
 // store_staged_rows: the wave's NROWS staged rows back out, G::kCPR lanes per row, so that one
-// store covers 64 / kCPR consecutive rows (1 KiB at D = 128). Rows from `nvalid` on are not
-// stored.
+// store covers 64 / kCPR rows (1 KiB at D = 128, consecutive where `stride`, the elements from
+// one row of O to the next, is D). Rows from `nvalid` on are not stored.
 template <int D, int NROWS>
-__device__ __forceinline__ void store_staged_rows(uint16_t* obase, const char* st, int nvalid,
-                                                  int lane) {
+__device__ __forceinline__ void store_staged_rows(uint16_t* obase, size_t stride, const char* st,
+                                                  int nvalid, int lane) {
   using G = Geo<D, 4>;
   static_assert(NROWS % (64 / G::kCPR) == 0, "whole stores");
   constexpr int kRowsPerStore = 64 / G::kCPR;
@@ -312,7 +312,7 @@ __device__ __forceinline__ void store_staged_rows(uint16_t* obase, const char* s
   for (int i = 0; i < NROWS / kRowsPerStore; ++i) {
     const int r = kRowsPerStore * i + lane / G::kCPR;
     const u32x4 x = *reinterpret_cast<const u32x4*>(st + r * G::kRow + ((cc ^ kswz<D>(r)) * 16));
-    if (r < nvalid) *reinterpret_cast<u32x4*>(obase + (size_t)r * D + cc * 8) = x;
+    if (r < nvalid) *reinterpret_cast<u32x4*>(obase + (size_t)r * stride + cc * 8) = x;
   }
 }
 

@@ -3,9 +3,9 @@
 libattn_poison.so is the same sources compiled with -DATTN_POISON_LDS: every kernel first fills
 the LDS arrays it uses with 0xff bytes (NaN as fp32 and as bf16). The kernels are written so
 that no output depends on an LDS byte they did not write themselves: K/V stages past a context
-or past Sk, stages that staged Q before their first tile, the dummy block before a wide loop's
-first, decode slots of blocks outside the pool. So both builds must give the same bits on every
-output, here for every kernel family of the library: the wide forward (with key-range splits
+or past Sk, stages that staged Q before their first tile or O after their last, the dummy block
+before a wide loop's first, decode slots of blocks outside the pool. So both builds must give
+the same bits on every output, here for every kernel family of the library: the wide forward (with key-range splits
 and cross-XCD item taking), the paired-tile and the tile forwards, the fp32 forward, the paged
 prefill, the paged decode, RoPE + cache store and the residual-add RMS norm. A difference
 means a read of a byte no instruction of the kernel wrote (a race, or a missing clear), which
@@ -143,6 +143,17 @@ def test_paged_prefill_bits_match(case, dev, libs):
     mq, mk = max(1, max(ql)), max(kl)
     a, b = both(libs, lambda: A.attn_fwd_paged(*t, mq, mk, causal=causal))
     assert_same_bits(a, b, f"attn_fwd_paged {case}")
+
+
+def test_paged_prefill_wrap_bits_match(dev, libs):
+    """max_q below a chunk's length: each workgroup computes several query tiles in turn, and
+    the stages that held one tile's O are loaded again for the next."""
+    x = W.paged_prefill_inputs(8, 2, 128, (700, 20), (900, 4000), seed=7250, poison="nan")
+    t = (bf(x.q, dev), bf(x.k_cache, dev), bf(x.v_cache, dev), i32(x.block_table, dev),
+         i32(x.cu_seqlens_q, dev), i32(x.ctx_lens, dev))
+    for causal in (True, False):
+        a, b = both(libs, lambda: A.attn_fwd_paged(*t, 128, 4000, causal=causal))
+        assert_same_bits(a, b, f"attn_fwd_paged max_q=128 causal={causal}")
 
 
 @pytest.mark.parametrize("workers", [0, 100])
